@@ -1,0 +1,159 @@
+"""CPU oracle of the Medusa verify step -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the package smoke check and the bench's CPU-baseline leg may
+import this package.  It wraps the plain fp64 C reference in
+medusa_oracle.c (built with gcc, OpenMP over independent outputs) with NumPy
+in/out.  Nothing here is shared with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "medusa_oracle.c")
+_LIB = os.path.join(_HERE, "libmedusa_oracle.so")
+
+DTYPE_CODE = {"f32": 0, "bf16": 1}
+MODE_CODE = {"greedy": 0, "typical": 1}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library in place (gcc, -O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        L.oracle_heads_topk.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
+        L.oracle_tree.argtypes = [P, P, I, I, I, P, P, P]
+        L.oracle_tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P, I, P]
+        L.oracle_tree_accept.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, D, D,
+                                         P, P, P, P, P, P, P, P]
+        L.oracle_num_threads.argtypes = []
+        for f in ("oracle_heads_topk", "oracle_tree", "oracle_tree_attention",
+                  "oracle_tree_accept", "oracle_num_threads"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a: np.ndarray, dt) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def _stored(a: np.ndarray, dtype: str) -> np.ndarray:
+    return _c(a, np.uint16 if dtype == "bf16" else np.float32)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+def heads_topk(hidden, w1, w2, s: int, dtype: str) -> Dict[str, np.ndarray]:
+    hidden, w1, w2 = (_stored(x, dtype) for x in (hidden, w1, w2))
+    B, d = hidden.shape
+    K, V = w2.shape[0], w2.shape[1]
+    z = np.empty((B, K, d), np.float64)
+    logits = np.empty((B, K, V), np.float64)
+    ids = np.empty((B, K, s), np.int32)
+    vals = np.empty((B, K, s), np.float64)
+    rc = lib().oracle_heads_topk(_p(hidden), _p(w1), _p(w2), B, K, d, V, s, DTYPE_CODE[dtype],
+                                 _p(z), _p(logits), _p(ids), _p(vals))
+    _check(rc, "oracle_heads_topk")
+    return {"z": z, "logits": logits, "topk_ids": ids, "topk_vals": vals}
+
+
+def tree(parent, K: int, s: int, node_rank=None) -> Dict[str, np.ndarray]:
+    parent = _c(parent, np.int32)
+    T = parent.shape[0]
+    nr = None if node_rank is None else _c(node_rank, np.int32)
+    W = (T + 63) // 64
+    depth = np.empty(T, np.int32)
+    rank = np.empty(T, np.int32)
+    mask = np.empty((T, W), np.uint64)
+    rc = lib().oracle_tree(_p(parent), _p(nr), T, K, s, _p(depth), _p(rank), _p(mask))
+    _check(rc, "oracle_tree")
+    return {"depth": depth, "rank": rank, "mask": mask}
+
+
+def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, parent, scale: float,
+                   dtype: str, rows=None) -> np.ndarray:
+    """Returns [B][Hq][T][dh] fp64, or [nrows][dh] when rows (n x 3) is given."""
+    q, k_cache, v_cache, k_tree, v_tree = (_stored(x, dtype)
+                                           for x in (q, k_cache, v_cache, k_tree, v_tree))
+    prefix_len = _c(prefix_len, np.int32)
+    parent = _c(parent, np.int32)
+    B, Hq, T, dh = q.shape
+    Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
+    if rows is not None:
+        rows = _c(rows, np.int32).reshape(-1, 3)
+        out = np.empty((rows.shape[0], dh), np.float64)
+        nrows = rows.shape[0]
+    else:
+        out = np.empty((B, Hq, T, dh), np.float64)
+        nrows = 0
+    rc = lib().oracle_tree_attention(_p(q), _p(k_cache), _p(v_cache), _p(prefix_len), _p(k_tree),
+                                     _p(v_tree), _p(parent), B, Hq, Hkv, Lcap, dh, T, float(scale),
+                                     DTYPE_CODE[dtype], _p(rows), nrows, _p(out))
+    _check(rc, "oracle_tree_attention")
+    return out
+
+
+def tree_accept(logits, topk_ids, parent, dtype: str, mode: str, temperature: float = 1.0,
+                eps: float = 0.09, delta: float = 0.6, node_rank=None) -> Dict[str, np.ndarray]:
+    logits = _stored(logits, dtype)
+    topk_ids = _c(topk_ids, np.int32)
+    parent = _c(parent, np.int32)
+    nr = None if node_rank is None else _c(node_rank, np.int32)
+    B, T, V = logits.shape
+    K, s = topk_ids.shape[1], topk_ids.shape[2]
+    out = {
+        "accept_len": np.empty(B, np.int32),
+        "best_node": np.empty(B, np.int32),
+        "accepted_tokens": np.empty((B, K), np.int32),
+        "node_tokens": np.empty((B, T), np.int32),
+        "next_token": np.empty(B, np.int32),
+        "valid": np.empty((B, T), np.uint8),
+        "ratio": np.empty((B, T), np.float64),
+        "entropy": np.empty((B, T), np.float64),
+    }
+    rc = lib().oracle_tree_accept(_p(logits), _p(topk_ids), _p(parent), _p(nr), B, T, V, K, s,
+                                  DTYPE_CODE[dtype], MODE_CODE[mode], float(temperature),
+                                  float(eps), float(delta), _p(out["accept_len"]),
+                                  _p(out["best_node"]), _p(out["accepted_tokens"]),
+                                  _p(out["node_tokens"]), _p(out["next_token"]), _p(out["valid"]),
+                                  _p(out["ratio"]), _p(out["entropy"]))
+    _check(rc, "oracle_tree_accept")
+    return out

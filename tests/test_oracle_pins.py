@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a library routine, a closed form, a
+brute-force restatement or a hand-derived case, chosen so that a plausible
+mistake (a dropped residual, a ReLU for the SiLU, a transposed weight, a
+mask without self, a wrong tie-break, a missing temperature) fails one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from medusa_tree_verification_amd import workloads as W
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- heads
+def test_heads_w1_zero_is_plain_gemv():
+    """W1 = 0 makes SiLU(0) + h = h, so logits = W2 h (numpy GEMV)."""
+    rng = np.random.default_rng(1)
+    B, K, d, V, s = 2, 3, 32, 50, 4
+    h = rng.standard_normal((B, d)).astype(np.float32)
+    w1 = np.zeros((K, d, d), np.float32)
+    w2 = rng.standard_normal((K, V, d)).astype(np.float32)
+    out = oracle.heads_topk(h, w1, w2, s, "f32")
+    ref = np.einsum("kvd,bd->bkv", w2.astype(np.float64), h.astype(np.float64))
+    np.testing.assert_allclose(out["logits"], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(out["z"], np.broadcast_to(h[:, None, :], (B, K, d)))
+
+
+def test_heads_silu_and_residual_closed_forms():
+    """W1 = c*I gives u = c h.  With SiLU(x) = x*sigmoid(x):
+    z(h) - z(-h) = c h + 2 h   (odd part of SiLU is x/2, plus the residual)
+    z(h) + z(-h) = c h tanh(c h / 2)   (even part)."""
+    rng = np.random.default_rng(2)
+    d, c = 16, 0.75
+    h = rng.standard_normal(d).astype(np.float32) * 3
+    hb = np.stack([h, -h])
+    w1 = (c * np.eye(d, dtype=np.float32))[None]
+    w2 = np.eye(d, dtype=np.float32)[None]  # logits = z
+    out = oracle.heads_topk(hb, w1, w2, 1, "f32")
+    z = out["z"][:, 0, :]
+    x = c * h.astype(np.float64)
+    np.testing.assert_allclose(z[0] - z[1], x + 2 * h, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(z[0] + z[1], x * np.tanh(x / 2), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(out["logits"][:, 0, :], z, rtol=0, atol=0)
+
+
+def test_heads_weight_orientation_out_in():
+    """torch Linear convention [out][in]: W1[j][k] = 1 makes u_j = h_k, and
+    W2[v][j] = 1 makes logit_v = z_j."""
+    d, V = 8, 5
+    h = np.arange(1, d + 1, dtype=np.float32)
+    w1 = np.zeros((1, d, d), np.float32)
+    w1[0, 2, 6] = 1.0  # u_2 = h_6 = 7
+    w2 = np.zeros((1, V, d), np.float32)
+    w2[0, 4, 2] = 1.0  # logit_4 = z_2
+    out = oracle.heads_topk(h[None], w1, w2, 1, "f32")
+    z = out["z"][0, 0]
+    u2 = 7.0
+    assert abs(z[2] - (u2 / (1 + math.exp(-u2)) + 3.0)) < 1e-12
+    others = np.delete(np.arange(d), 2)
+    np.testing.assert_array_equal(z[others], h[others])  # SiLU(0) = 0
+    assert out["logits"][0, 0, 4] == z[2]
+    assert out["topk_ids"][0, 0, 0] == 4
+
+
+def test_heads_topk_matches_sort_with_ties():
+    """Top-s = first s of a stable sort by (value desc, id asc); ties planted."""
+    rng = np.random.default_rng(3)
+    B, K, d, V, s = 3, 2, 8, 40, 6
+    h = np.zeros((B, d), np.float32)
+    h[:, 0] = 1.0
+    w1 = np.zeros((K, d, d), np.float32)
+    # logits = W2[:, :, 0] exactly; use small integers so ties are exact
+    w2 = np.zeros((K, V, d), np.float32)
+    w2[:, :, 0] = rng.integers(-3, 4, size=(K, V)).astype(np.float32)
+    out = oracle.heads_topk(h, w1, w2, s, "f32")
+    for b in range(B):
+        for k in range(K):
+            row = w2[k, :, 0].astype(np.float64)
+            order = np.lexsort((np.arange(V), -row))[:s]
+            np.testing.assert_array_equal(out["topk_ids"][b, k], order)
+            np.testing.assert_array_equal(out["topk_vals"][b, k], row[order])
+
+
+def test_heads_bf16_single_rounding_point():
+    """bf16 mode rounds z once (fp64 -> fp32 -> bf16, nearest-even, checked
+    with torch's own conversion) and keeps logits unrounded (= W2 z)."""
+    rng = np.random.default_rng(4)
+    B, K, d, V, s = 2, 2, 64, 30, 3
+    hb = W.encode(rng.standard_normal((B, d)), W.BF16)
+    w1b = W.encode(rng.standard_normal((K, d, d)) * 0.1, W.BF16)
+    w2b = W.encode(rng.standard_normal((K, V, d)) * 0.1, W.BF16)
+    ob = oracle.heads_topk(hb, w1b, w2b, s, "bf16")
+    # same values in fp32 mode: unrounded z
+    of = oracle.heads_topk(W.decode(hb, W.BF16).astype(np.float32),
+                           W.decode(w1b, W.BF16).astype(np.float32),
+                           W.decode(w2b, W.BF16).astype(np.float32), s, "f32")
+    z_ref = torch.from_numpy(of["z"].astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(ob["z"], z_ref)
+    assert not np.array_equal(of["z"], ob["z"])  # the rounding point exists
+    w2d = W.decode(w2b, W.BF16)
+    np.testing.assert_allclose(ob["logits"], np.einsum("kvd,bkd->bkv", w2d, ob["z"]),
+                               rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ tree
+@pytest.mark.parametrize("K,s,T", [(3, 2, 15), (4, 3, 121), (2, 3, 13), (1, 1, 2)])
+def test_full_product_counts(K, s, T):
+    """The uncut product has sum_{j<=K} s^j nodes (k=4, s=3: 81 leaf paths)."""
+    t = W.full_product_tree(K, s)
+    assert t.T == T == sum(s ** j for j in range(K + 1))
+    o = oracle.tree(t.parent, K, s)
+    assert np.bincount(o["depth"]).tolist() == [s ** j for j in range(K + 1)]
+    assert int((o["depth"] == K).sum()) == s ** K
+
+
+def test_default_pruned_trees():
+    """63 candidates + root for the 4-head tree; 255 + root for 5 heads."""
+    t64 = W.pruned_tree(W.WORKLOADS["llama7b_b1"].rates, 3, 64)
+    assert np.bincount(oracle.tree(t64.parent, 4, 3)["depth"]).tolist() == [1, 3, 9, 25, 26]
+    t256 = W.pruned_tree(W.WORKLOADS["large_vocab_typical"].rates, 3, 256)
+    assert np.bincount(oracle.tree(t256.parent, 5, 3)["depth"]).tolist() == [1, 3, 9, 27, 81, 135]
+
+
+def _trees():
+    out = [W.full_product_tree(3, 2), W.full_product_tree(4, 3), W.chain_tree(5),
+           W.pruned_tree(W.WORKLOADS["llama7b_b1"].rates, 3, 64),
+           W.pruned_tree(W.WORKLOADS["large_vocab_typical"].rates, 3, 256),
+           W.tree_from_paths([()])]
+    out += [W.random_tree(100 + i, T, 6, 4) for i, T in enumerate([2, 7, 33, 65, 129])]
+    return out
+
+
+@pytest.mark.parametrize("ti", range(11))
+def test_tree_mask_and_ranks_against_rank_tuples(ti):
+    """Mask row n = ancestors-or-self of n, found independently from the
+    rank tuples (prefix relation); rank = last tuple entry; depth = length."""
+    t = _trees()[ti]
+    K = max(len(p) for p in t.paths)
+    s = max([p[-1] for p in t.paths if p] + [0]) + 1
+    o = oracle.tree(t.parent, K, s)
+    T = t.T
+    for n in range(T):
+        assert o["depth"][n] == len(t.paths[n])
+        if n:
+            assert o["rank"][n] == t.paths[n][-1]
+        bits = set(j for j in range(T) if (int(o["mask"][n, j // 64]) >> (j % 64)) & 1)
+        ref = set(m for m in range(T) if brute.is_prefix(t.paths[m], t.paths[n]))
+        assert bits == ref
+        assert len(bits) == len(t.paths[n]) + 1          # popcount = depth + 1
+        assert max(bits) == n                           # lower-triangular, self included
+        if n:
+            pbits = set(j for j in range(T)
+                        if (int(o["mask"][t.parent[n], j // 64]) >> (j % 64)) & 1)
+            assert bits == pbits | {n}                  # mask(n) = {n} U mask(parent)
+
+
+def test_tree_rejects_bad_parent_arrays():
+    with pytest.raises(oracle.OracleError):
+        oracle.tree(np.array([0, 0], np.int32), 2, 2)      # root must be -1
+    with pytest.raises(oracle.OracleError):
+        oracle.tree(np.array([-1, 1], np.int32), 2, 2)     # not parent-before-child
+    with pytest.raises(oracle.OracleError):
+        oracle.tree(np.array([-1, 0, 1, 2], np.int32), 2, 2)  # depth 3 > K
+    with pytest.raises(oracle.OracleError):
+        oracle.tree(np.array([-1, 0, 0, 0], np.int32), 3, 2)  # rank 2 >= s
+    with pytest.raises(oracle.OracleError):
+        oracle.tree(np.array([-1, 0, 0], np.int32), 2, 2, node_rank=np.array([0, 1, 1]))
+
+
+# ------------------------------------------------------------- attention
+def _attn_inputs(seed, B, Hq, Hkv, T, dh, Lcap, L):
+    rng = np.random.default_rng(seed)
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    return dict(q=f(B, Hq, T, dh), k_cache=f(B, Hkv, Lcap, dh), v_cache=f(B, Hkv, Lcap, dh),
+                k_tree=f(B, Hkv, T, dh), v_tree=f(B, Hkv, T, dh),
+                prefix_len=np.asarray(L, np.int32))
+
+
+@pytest.mark.parametrize("tree_kind", ["full", "random", "pruned"])
+def test_attention_equals_per_path_causal_attention(tree_kind):
+    """Tree-masked attention of node t == ordinary causal attention over the
+    flat sequence prefix + (root..t path), read at its last position: what the
+    tree mask buys is verifying every path in one pass."""
+    if tree_kind == "full":
+        t = W.full_product_tree(3, 2)
+    elif tree_kind == "random":
+        t = W.random_tree(7, 20, 5, 3)
+    else:
+        t = W.pruned_tree(W.WORKLOADS["llama7b_b1"].rates, 3, 64)
+    B, Hq, Hkv, dh, Lcap = 2, 4, 2, 8, 9
+    L = [9, 4]
+    x = _attn_inputs(11, B, Hq, Hkv, t.T, dh, Lcap, L)
+    scale = 1 / math.sqrt(dh)
+    out = oracle.tree_attention(**x, parent=t.parent, scale=scale, dtype="f32")
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            for n in range(t.T):
+                path = brute.path_nodes(t.paths, n)
+                ks = np.concatenate([x["k_cache"][b, kv, :L[b]], x["k_tree"][b, kv, path]])
+                vs = np.concatenate([x["v_cache"][b, kv, :L[b]], x["v_tree"][b, kv, path]])
+                qs = np.concatenate([np.zeros((L[b], dh)), x["q"][b, h, path]])  # only last row used
+                ref = brute.causal_attention_last(qs.astype(np.float64), ks.astype(np.float64),
+                                                  vs.astype(np.float64), scale)
+                np.testing.assert_allclose(out[b, h, n], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_chain_tree_is_causal_sdpa():
+    """A chain tree (s = 1) is plain causal attention: torch SDPA, fp64."""
+    K, dh, L = 6, 16, 11
+    t = W.chain_tree(K)
+    x = _attn_inputs(12, 1, 2, 2, t.T, dh, L, [L])
+    out = oracle.tree_attention(**x, parent=t.parent, scale=1 / math.sqrt(dh), dtype="f32")
+    for h in range(2):
+        k = np.concatenate([x["k_cache"][0, h], x["k_tree"][0, h]]).astype(np.float64)
+        v = np.concatenate([x["v_cache"][0, h], x["v_tree"][0, h]]).astype(np.float64)
+        q = np.concatenate([np.zeros((L, dh)), x["q"][0, h]]).astype(np.float64)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            is_causal=True)[0, L:].numpy()
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_single_node_is_decode_attention():
+    """T = 1: one query over prefix + itself (torch SDPA, no mask)."""
+    dh, L = 32, 40
+    x = _attn_inputs(13, 1, 1, 1, 1, dh, L, [L])
+    out = oracle.tree_attention(**x, parent=np.array([-1], np.int32), scale=0.3, dtype="f32")
+    k = np.concatenate([x["k_cache"][0, 0], x["k_tree"][0, 0]]).astype(np.float64)
+    v = np.concatenate([x["v_cache"][0, 0], x["v_tree"][0, 0]]).astype(np.float64)
+    q = x["q"][0, 0].astype(np.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        scale=0.3)[0].numpy()
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    """q = 0 -> mean of the visible v rows; all v equal -> that row;
+    prefix length 0 -> ancestors only; prefix longer than the cache is clamped."""
+    t = W.full_product_tree(2, 3)
+    dh, Lcap = 8, 5
+    x = _attn_inputs(14, 3, 2, 2, t.T, dh, Lcap, [5, 0, 99])
+    x["q"][:] = 0
+    out = oracle.tree_attention(**x, parent=t.parent, scale=0.5, dtype="f32")
+    for b, L in enumerate([5, 0, 5]):
+        for n in range(t.T):
+            path = brute.path_nodes(t.paths, n)
+            vis = np.concatenate([x["v_cache"][b, 0, :L], x["v_tree"][b, 0, path]])
+            np.testing.assert_allclose(out[b, 0, n], vis.astype(np.float64).mean(0), rtol=1e-12,
+                                       atol=1e-12)
+    y = _attn_inputs(15, 1, 1, 1, t.T, dh, Lcap, [3])
+    y["v_cache"][:] = y["v_tree"][:] = np.arange(dh, dtype=np.float32)
+    out = oracle.tree_attention(**y, parent=t.parent, scale=0.5, dtype="f32")
+    np.testing.assert_allclose(out[0, 0], np.broadcast_to(np.arange(dh), (t.T, dh)), rtol=1e-12)
+
+
+def test_attention_rows_subset_matches_full():
+    t = W.full_product_tree(2, 2)
+    x = _attn_inputs(16, 2, 4, 2, t.T, 8, 6, [6, 3])
+    full = oracle.tree_attention(**x, parent=t.parent, scale=0.35, dtype="f32")
+    rows = np.array([[1, 3, 6], [0, 0, 0], [1, 1, 2]], np.int32)
+    sub = oracle.tree_attention(**x, parent=t.parent, scale=0.35, dtype="f32", rows=rows)
+    for i, (b, h, n) in enumerate(rows):
+        np.testing.assert_array_equal(sub[i], full[b, h, n])
+
+
+# ------------------------------------------------------------ acceptance
+def test_typical_hand_cases():
+    g = json.load(open(os.path.join(GOLDEN, "typical_acceptance_cases.json")))
+    for c in g["cases"]:
+        p = np.array(c["p"], np.float64)
+        V = len(p)
+        logits = np.where(p > 0, np.log(np.maximum(p, 1e-300)), -1e4).astype(np.float32)
+        # root with V children at depth 1; child r carries token r
+        parent = np.array([-1] + [0] * V, np.int32)
+        ids = np.arange(V, dtype=np.int32).reshape(1, 1, V)
+        L = np.zeros((1, V + 1, V), np.float32)
+        L[0, 0] = logits
+        o = oracle.tree_accept(L, ids, parent, "f32", "typical", temperature=1.0,
+                               eps=g["eps"], delta=g["delta"])
+        acc = [r for r in range(V) if o["valid"][0, 1 + r]]
+        assert acc == c["accepted"], c["name"]
+        assert abs(o["entropy"][0, 0] - c["H"]) < 1e-6, c["name"]
+        thr = min(g["eps"], g["delta"] * math.exp(-o["entropy"][0, 0]))
+        assert abs(thr - c["threshold"]) < 1e-6, c["name"]
+        assert o["accept_len"][0] == (1 if acc else 0)
+        assert o["best_node"][0] == (1 + acc[0] if acc else 0)
+
+
+def test_typical_temperature_scales_logits():
+    """softmax(logits / T): logits 2*ln p at T = 2 gives back p."""
+    p = np.array([0.7, 0.2, 0.06, 0.04])
+    parent = np.array([-1, 0, 0, 0, 0], np.int32)
+    ids = np.arange(4, dtype=np.int32).reshape(1, 1, 4)
+    L = np.zeros((1, 5, 4), np.float32)
+    L[0, 0] = 2 * np.log(p)
+    o = oracle.tree_accept(L, ids, parent, "f32", "typical", temperature=2.0)
+    assert [r for r in range(4) if o["valid"][0, 1 + r]] == [0, 1]
+    assert abs(o["entropy"][0, 0] - 0.86912) < 1e-5
+    o1 = oracle.tree_accept(L, ids, parent, "f32", "typical", temperature=1.0)
+    assert o1["entropy"][0, 0] < 0.8  # sharper at T = 1
+
+
+def test_greedy_argmax_and_ties():
+    """Greedy: child valid iff its token is the parent row's argmax; equal
+    maxima resolve to the smaller token id."""
+    parent = np.array([-1, 0, 0, 0], np.int32)
+    ids = np.array([[[5, 2, 7]]], np.int32)
+    L = np.zeros((1, 4, 8), np.float32)
+    L[0, 0, [2, 5]] = 3.0   # tie between tokens 2 and 5 -> 2
+    o = oracle.tree_accept(L, ids, parent, "f32", "greedy")
+    assert o["valid"][0].tolist() == [1, 0, 1, 0]
+    assert o["accept_len"][0] == 1 and o["best_node"][0] == 2
+    assert o["accepted_tokens"][0].tolist() == [2]
+    assert o["next_token"][0] == 0  # leaf row all zeros -> token 0
+
+
+def test_stop_at_first_failure_on_a_chain():
+    """Verification along a path stops at the first rejected token."""
+    t = W.chain_tree(4)
+    ids = np.array([[[3], [1], [4], [1]]], np.int32)
+    L = np.zeros((1, 5, 6), np.float32)
+    for n, tok in enumerate([3, 1, 0, 1]):   # depth-3 candidate 4 is not the argmax
+        L[0, n, tok] = 1.0
+    o = oracle.tree_accept(L, ids, t.parent, "f32", "greedy")
+    assert o["valid"][0].tolist() == [1, 1, 1, 0, 1]
+    assert o["accept_len"][0] == 2 and o["best_node"][0] == 2
+    assert o["accepted_tokens"][0].tolist() == [3, 1, -1, -1]
+    assert o["next_token"][0] == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_matches_path_enumeration(seed):
+    """Random trees and logits: the oracle's (accept_len, best_node, tokens)
+    equal brute-force enumeration of all root..node paths, given the valid
+    bits; valid bits equal a direct argmax check (greedy)."""
+    rng = np.random.default_rng(seed)
+    K, s, V, B = 5, 3, 6, 4
+    t = W.random_tree(200 + seed, 30, K, s)
+    ids = np.stack([np.stack([rng.choice(V, s, replace=False) for _ in range(K)])
+                    for _ in range(B)]).astype(np.int32)
+    L = rng.integers(0, 3, size=(B, t.T, V)).astype(np.float32)  # many ties
+    o = oracle.tree_accept(L, ids, t.parent, "f32", "greedy")
+    tok = W.path_tokens(t, ids)
+    np.testing.assert_array_equal(o["node_tokens"], tok)
+    for b in range(B):
+        for n in range(1, t.T):
+            row = L[b, t.parent[n]]
+            am = int(np.flatnonzero(row == row.max())[0])
+            assert o["valid"][b, n] == (tok[b, n] == am)
+        best, dep = brute.accept_by_paths(t.paths, o["valid"][b])
+        assert (o["best_node"][b], o["accept_len"][b]) == (best, dep)
+        path = brute.path_nodes(t.paths, best)[1:]
+        exp_tokens = [tok[b, m] for m in path] + [-1] * (K - len(path))
+        assert o["accepted_tokens"][b].tolist() == exp_tokens
+        assert o["next_token"][b] == int(np.argmax(L[b, best]))
+
+
+def test_accept_bf16_decoding_matches_f32():
+    """bf16 logits are decoded exactly: same result as their fp32 values."""
+    rng = np.random.default_rng(9)
+    t = W.full_product_tree(2, 3)
+    ids = np.array([[[1, 2, 3], [4, 5, 6]]], np.int32)
+    Lb = W.encode(rng.standard_normal((1, t.T, 10)), W.BF16)
+    a = oracle.tree_accept(Lb, ids, t.parent, "bf16", "typical", temperature=0.7)
+    b = oracle.tree_accept(W.decode(Lb, W.BF16).astype(np.float32), ids, t.parent, "f32",
+                           "typical", temperature=0.7)
+    for k in ("valid", "accept_len", "best_node", "accepted_tokens", "next_token"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ------------------------------------------------------- workload recipe
+@pytest.mark.parametrize("name", ["ragged_b16_gqa_typical"])
+def test_typical_workload_entropy_spread(name):
+    """The typical-mode recipe spreads row entropies over about 0.5-5 nats."""
+    wl = W.WORKLOADS[name]
+    t = W.workload_tree(wl)
+    ids = W.candidate_table(1000 * wl.cid + 12, wl.B, wl.K, wl.s, wl.V)
+    tok = W.path_tokens(t, ids)
+    logits = W.verify_logits(wl, t, tok)
+    o = oracle.tree_accept(logits, ids, t.parent, wl.dtype, "typical", wl.temperature)
+    H = o["entropy"][np.isfinite(o["entropy"])]
+    assert H.min() < 1.0 and H.max() > 4.0, (H.min(), H.max())
+    # decisions are not knife-edge: every child's p/threshold is off 1 by > 1e-3
+    r = o["ratio"][:, 1:]
+    assert np.all(np.abs(r - 1) > 1e-3)
+    assert 0 < o["accept_len"].mean() < wl.K
