@@ -1,0 +1,198 @@
+/*
+ * medusa_verify.h -- C ABI of the MI355X (gfx950) Medusa verify step.
+ *
+ * One Medusa decode step verifies, in a single pass, the candidate tokens
+ * proposed by K extra decoding heads on the base model's last hidden state
+ * ("Medusa: Simple LLM Inference Acceleration Framework with Multiple
+ * Decoding Heads", paper explainer page: head architecture, tree attention,
+ * typical acceptance).  The library exports the three compute calls of that
+ * step, all asynchronous on a caller-supplied HIP stream:
+ *
+ *   medusa_heads_topk  K heads H_i(h) = W2_i (SiLU(W1_i h) + h) + top-s
+ *   tree_attention     every tree node attends to the KV prefix plus its own
+ *                      ancestors (and itself) -- one pass over the tree
+ *   tree_accept        greedy or typical acceptance of the longest valid path
+ *
+ * Conventions (all calls):
+ *  - Every pointer marked "device" is device memory on the current HIP
+ *    device; "host" pointers are read during the call only.  The caller owns
+ *    all memory; the library never allocates, frees or synchronises.
+ *  - Tensors are dense, row-major, with the shapes written next to them.
+ *    Weights are [out][in] (torch.nn.Linear layout).  Element type is given
+ *    by `dtype`: MEDUSA_F32 (IEEE binary32) or MEDUSA_BF16 (bfloat16, the
+ *    upper 16 bits of a binary32).  Index tensors are int32.
+ *  - `stream` is a hipStream_t (NULL = the null stream).
+ *  - Scratch memory comes from the caller's workspace `ws` of `ws_bytes`
+ *    bytes (device, 256-byte aligned), sized by the matching
+ *    *_workspace_bytes() call.  Its contents need no initialisation and are
+ *    undefined after the call.  Calls that share a workspace must be
+ *    ordered on one stream.
+ *  - Return value: MEDUSA_OK, or a negative medusa_status.  Argument errors
+ *    are detected on the host before anything is enqueued; no output is
+ *    touched then.  MEDUSA_ERR_LAUNCH reports a failed kernel launch.
+ *  - The library holds no global state and is safe to call from several
+ *    host threads (on different workspaces).
+ */
+#ifndef MEDUSA_VERIFY_H
+#define MEDUSA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_accept_mode;
+
+typedef enum {
+    MEDUSA_OK = 0,
+    MEDUSA_ERR_NULL = -1,      /* a required pointer is NULL              */
+    MEDUSA_ERR_SHAPE = -2,     /* a size is out of the supported range    */
+    MEDUSA_ERR_DTYPE = -3,     /* unknown dtype                           */
+    MEDUSA_ERR_TREE = -4,      /* parent / node_rank array is not a valid tree */
+    MEDUSA_ERR_WORKSPACE = -5, /* workspace missing, misaligned or too small */
+    MEDUSA_ERR_PARAM = -6,     /* bad scalar (mode, temperature, eps, delta, scale) */
+    MEDUSA_ERR_LAUNCH = -7     /* a kernel launch failed                  */
+} medusa_status;
+
+/* Supported ranges (checked on the host). */
+#define MEDUSA_MAX_BATCH 16     /* heads: B <= 16 (one MFMA column tile) */
+#define MEDUSA_MAX_HEADS 16     /* K                                      */
+#define MEDUSA_MAX_TOPS 8       /* s                                      */
+#define MEDUSA_MAX_TREE 256     /* T, nodes including the root            */
+
+/* ------------------------------------------------------------------------
+ * medusa_heads_topk -- the K Medusa heads and their top-s candidates.
+ *
+ * Head equation of the paper explainer page (section "Medusa Head
+ * architecture"): H_i(h) = W2_i (SiLU(W1_i h) + h), SiLU(x) = x*sigmoid(x),
+ * W1_i: d -> d, W2_i: d -> V, no biases (its PyTorch head listing); every
+ * head reads the same hidden state h.  Then the s largest logits of every
+ * (sequence, head), as candidate tokens for tree depth i+1 (same page,
+ * "tree attention": top-s per head, s = 3 recommended).
+ *
+ *   hidden     device [B][d]        dtype
+ *   w1         device [K][d][d]     dtype   ([out][in])
+ *   w2         device [K][V][d]     dtype   ([out][in])
+ *   logits_out device [B][K][V]     float32, or NULL to skip writing logits
+ *   topk_ids   device [B][K][s]     int32: larger logit first, equal logits
+ *                                   ordered by smaller token id
+ *   topk_vals  device [B][K][s]     float32 logits of topk_ids, or NULL
+ *
+ * Arithmetic: fp32 accumulation.  In BF16 mode the W2 input
+ * z = SiLU(W1 h) + h is rounded once to bf16 (nearest-even); logits are
+ * fp32 and not rounded.  Limits: 1 <= B <= 16, 1 <= K <= 16,
+ * 128 <= d <= 16384 with d % 128 == 0, s <= V, 1 <= s <= 8.
+ * Kernels: stage 1 (W1 stream + SiLU + residual -> z in the workspace),
+ * stage 2 (W2 stream on the matrix cores, fused top-s, last-arriving
+ * workgroup of each head merges the per-workgroup lists).
+ * ---------------------------------------------------------------------- */
+int medusa_heads_topk(const void *hidden, const void *w1, const void *w2, int B, int K, int d,
+                      int V, int s, int dtype, float *logits_out, int32_t *topk_ids,
+                      float *topk_vals, void *ws, size_t ws_bytes, void *stream);
+
+/* The two stages of medusa_heads_topk as separate calls (same arguments and
+ * workspace; stage 2 must follow stage 1 on the same stream and workspace).
+ * medusa_heads_topk is exactly stage 1 followed by stage 2. */
+int medusa_heads_stage1(const void *hidden, const void *w1, int B, int K, int d, int V, int s,
+                        int dtype, void *ws, size_t ws_bytes, void *stream);
+int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, int s, int dtype,
+                        float *logits_out, int32_t *topk_ids, float *topk_vals, void *ws,
+                        size_t ws_bytes, void *stream);
+
+size_t medusa_heads_topk_workspace_bytes(int B, int K, int d, int V, int s, int dtype);
+
+/* ------------------------------------------------------------------------
+ * tree_attention -- one attention pass over the candidate tree.
+ *
+ * Tree-attention section of the paper explainer page: the candidates form
+ * a tree (pruned Cartesian product of the heads' top-s lists) and a mask
+ * lets each candidate attend only to its ancestors, so all paths are
+ * verified in one forward pass.  Read here as ancestor-or-self; every node
+ * also sees the whole KV-cache prefix of its sequence.
+ *
+ * Query row (b, h, t) -- sequence b, query head h, tree node t -- attends
+ * to prefix keys p < prefix_len[b] of kv head h / (Hq / Hkv) and to the tree
+ * keys of t's ancestors and t itself:
+ *   out[b][h][t] = sum_j softmax_j(scale * q.k_j) v_j.
+ *
+ *   q           device [B][Hq][T][dh]     dtype (post-rotary queries)
+ *   k_cache     device [B][Hkv][Lcap][dh] dtype
+ *   v_cache     device [B][Hkv][Lcap][dh] dtype
+ *   prefix_len  device [B] int32; values outside [0, Lcap] are clamped and
+ *               flagged in the workspace's first int32 (nonzero = clamped)
+ *   k_tree      device [B][Hkv][T][dh]    dtype (keys of the tree tokens)
+ *   v_tree      device [B][Hkv][T][dh]    dtype
+ *   parent      host [T] int32: parent[0] = -1, 0 <= parent[n] < n
+ *   out         device [B][Hq][T][dh]     dtype
+ *   mask_out    device [T][(T+63)/64] uint64 ancestor-or-self bit rows
+ *               (bit j of word j/64 of row n), or NULL
+ *
+ * Limits: T <= 256, dh in {64, 128}, Hq % Hkv == 0, Hq/Hkv*T rows,
+ * Lcap >= 0, scale > 0.  Arithmetic: MFMA (bf16 products, fp32
+ * accumulation; fp32 MFMA in F32 mode), online softmax in fp32.
+ * ---------------------------------------------------------------------- */
+int tree_attention(const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *prefix_len, const void *k_tree, const void *v_tree,
+                   const int32_t *parent, int B, int Hq, int Hkv, int Lcap, int dh, int T,
+                   float scale, int dtype, void *out, uint64_t *mask_out, void *ws,
+                   size_t ws_bytes, void *stream);
+
+size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int dh, int T,
+                                      int dtype);
+
+/* ------------------------------------------------------------------------
+ * tree_accept -- verify the candidates and keep the longest valid path.
+ *
+ * Node n > 0 carries token tok(n) = topk_ids[b][depth(n)-1][rank(n)], where
+ * rank(n) is node_rank[n] or, when node_rank is NULL, the number of earlier
+ * siblings of n.  Node c is checked against its parent's logits row
+ * (logits[b][parent(c)]):
+ *   MEDUSA_GREEDY  valid iff tok(c) is the row's argmax (equal maxima ->
+ *                  smaller id): temperature-0 verification by argmax
+ *                  comparison (explainer page, typical-acceptance section,
+ *                  last paragraph);
+ *   MEDUSA_TYPICAL p = softmax(row / temperature), H(p) = -sum p ln p,
+ *                  valid iff p(tok) > min(eps, delta * exp(-H)) (same
+ *                  section's inequality; its defaults eps = 0.09,
+ *                  delta = 0.6).
+ * The accepted path ends at the deepest node whose path from the root is
+ * all valid (the first rejection ends a path); equal depths -> lowest
+ * node index.
+ *
+ *   logits          device [B][T][V] dtype (the base model's logits at every
+ *                   tree node)
+ *   topk_ids        device [B][K][s] int32 (from medusa_heads_topk)
+ *   parent          host [T] int32 (as tree_attention)
+ *   node_rank       host [T] int32 or NULL
+ *   accept_len      device [B] int32: candidate tokens accepted, 0..K
+ *   best_node       device [B] int32: last node of the accepted path
+ *   accepted_tokens device [B][K] int32: tokens of the path, -1 padded
+ *   node_tokens     device [B][T] int32 or NULL: tok(n), root = -1
+ *   next_token      device [B] int32 or NULL: argmax of logits[b][best_node]
+ *
+ * Limits: T <= 256, depth <= K <= 16, rank < s <= 255, V >= 1; typical
+ * mode needs temperature > 0, 0 < eps, 0 < delta.
+ * ---------------------------------------------------------------------- */
+int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *parent,
+                const int32_t *node_rank, int B, int T, int V, int K, int s, int dtype, int mode,
+                float temperature, float eps, float delta, int32_t *accept_len,
+                int32_t *best_node, int32_t *accepted_tokens, int32_t *node_tokens,
+                int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
+
+size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s);
+
+/* Text for a medusa_status value (static storage). */
+const char *medusa_status_str(int status);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int medusa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_VERIFY_H */

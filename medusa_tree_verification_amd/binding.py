@@ -1,0 +1,201 @@
+"""Thin ctypes binding of libmedusa_verify.so (argument marshalling only).
+
+Every step of the verify path runs in the HIP kernels behind the C ABI in
+include/medusa_verify.h; these wrappers only turn torch tensors (device
+memory) into pointers, allocate outputs/workspace with torch and pass the
+current stream.  There is no other implementation: if the library is
+missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmedusa_verify.so")
+
+F32, BF16 = 0, 1
+GREEDY, TYPICAL = 0, 1
+
+STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "MEDUSA_ERR_DTYPE",
+          -4: "MEDUSA_ERR_TREE", -5: "MEDUSA_ERR_WORKSPACE", -6: "MEDUSA_ERR_PARAM",
+          -7: "MEDUSA_ERR_LAUNCH"}
+
+EXPORTS = ["medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2",
+           "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
+           "tree_accept", "tree_accept_workspace_bytes", "medusa_status_str", "medusa_abi_version"]
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}: {status_str(code)}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run medusa_tree_verification_amd/build.py "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.medusa_heads_topk.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    L.medusa_heads_stage1.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
+    L.medusa_heads_stage2.argtypes = [P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    L.medusa_heads_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.medusa_heads_topk_workspace_bytes.restype = Z
+    L.tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, Z, P]
+    L.tree_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    L.tree_attention_workspace_bytes.restype = Z
+    L.tree_accept.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, F, F, P, P, P, P, P, P, Z, P]
+    L.tree_accept_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.tree_accept_workspace_bytes.restype = Z
+    L.medusa_status_str.argtypes = [I]
+    L.medusa_status_str.restype = ctypes.c_char_p
+    L.medusa_abi_version.restype = I
+    for f in ("medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2", "tree_attention",
+              "tree_accept"):
+        getattr(L, f).restype = I
+    return L
+
+
+lib = _load()
+
+
+def status_str(code: int) -> str:
+    return lib.medusa_status_str(int(code)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MedusaError(fn, rc)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _host_i32(a: Optional[Sequence[int]]):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A device byte buffer (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def medusa_heads_topk(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, s: int, *,
+                      want_logits: bool = False, ws: Optional[torch.Tensor] = None,
+                      out: Optional[Dict[str, torch.Tensor]] = None,
+                      stream=None) -> Dict[str, torch.Tensor]:
+    for t, n in ((hidden, "hidden"), (w1, "w1"), (w2, "w2")):
+        _need(t, n)
+    B, d = hidden.shape
+    K, V = w2.shape[0], w2.shape[1]
+    dt = _dtype_code(hidden)
+    dev = hidden.device
+    if out is None:
+        out = {"topk_ids": torch.empty((B, K, s), dtype=torch.int32, device=dev),
+               "topk_vals": torch.empty((B, K, s), dtype=torch.float32, device=dev)}
+        if want_logits:
+            out["logits"] = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(lib.medusa_heads_topk_workspace_bytes(B, K, d, V, s, dt), dev)
+    rc = lib.medusa_heads_topk(_ptr(hidden), _ptr(w1), _ptr(w2), B, K, d, V, s, dt,
+                               _ptr(out.get("logits")), _ptr(out["topk_ids"]),
+                               _ptr(out.get("topk_vals")), _ptr(ws), ws.numel(), _stream(stream))
+    _check("medusa_heads_topk", rc)
+    return out
+
+
+def medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws, stream=None) -> None:
+    rc = lib.medusa_heads_stage1(_ptr(hidden), _ptr(w1), B, K, d, V, s, _dtype_code(hidden),
+                                 _ptr(ws), ws.numel(), _stream(stream))
+    _check("medusa_heads_stage1", rc)
+
+
+def medusa_heads_stage2(w2, B, K, d, V, s, topk_ids, ws, topk_vals=None, logits=None,
+                        stream=None) -> None:
+    rc = lib.medusa_heads_stage2(_ptr(w2), B, K, d, V, s, _dtype_code(w2), _ptr(logits),
+                                 _ptr(topk_ids), _ptr(topk_vals), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check("medusa_heads_stage2", rc)
+
+
+def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, parent, scale: float, *,
+                   want_mask: bool = False, ws: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                   stream=None):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (prefix_len, "prefix_len"),
+                 (k_tree, "k_tree"), (v_tree, "v_tree")):
+        _need(t, n)
+    B, Hq, T, dh = q.shape
+    Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    par, par_p = _host_i32(parent)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_mask and mask_out is None:
+        mask_out = torch.empty((T, (T + 63) // 64), dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = workspace(lib.tree_attention_workspace_bytes(B, Hq, Hkv, Lcap, dh, T, dt), dev)
+    rc = lib.tree_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(k_tree),
+                            _ptr(v_tree), par_p, B, Hq, Hkv, Lcap, dh, T, float(scale), dt,
+                            _ptr(out), _ptr(mask_out), _ptr(ws), ws.numel(), _stream(stream))
+    _check("tree_attention", rc)
+    return (out, mask_out) if want_mask else out
+
+
+def tree_accept(logits, topk_ids, parent, mode: int, temperature: float = 1.0, eps: float = 0.09,
+                delta: float = 0.6, node_rank=None, *, ws: Optional[torch.Tensor] = None,
+                out: Optional[Dict[str, torch.Tensor]] = None,
+                stream=None) -> Dict[str, torch.Tensor]:
+    _need(logits, "logits")
+    _need(topk_ids, "topk_ids")
+    B, T, V = logits.shape
+    K, s = topk_ids.shape[1], topk_ids.shape[2]
+    dt = _dtype_code(logits)
+    dev = logits.device
+    par, par_p = _host_i32(parent)
+    nr, nr_p = _host_i32(node_rank)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"accept_len": torch.empty(B, **i32), "best_node": torch.empty(B, **i32),
+               "accepted_tokens": torch.empty((B, K), **i32),
+               "node_tokens": torch.empty((B, T), **i32), "next_token": torch.empty(B, **i32)}
+    if ws is None:
+        ws = workspace(lib.tree_accept_workspace_bytes(B, T, V, K, s), dev)
+    rc = lib.tree_accept(_ptr(logits), _ptr(topk_ids), par_p, nr_p, B, T, V, K, s, dt, int(mode),
+                         float(temperature), float(eps), float(delta), _ptr(out["accept_len"]),
+                         _ptr(out["best_node"]), _ptr(out["accepted_tokens"]),
+                         _ptr(out.get("node_tokens")), _ptr(out.get("next_token")), _ptr(ws),
+                         ws.numel(), _stream(stream))
+    _check("tree_accept", rc)
+    return out

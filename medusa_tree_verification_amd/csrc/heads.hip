@@ -1,0 +1,494 @@
+// Medusa heads on gfx950: H_i(h) = W2_i (SiLU(W1_i h) + h) and per-head top-s.
+//
+// Head equation and bias-free two-Linear head: paper explainer page,
+// section "Medusa Head architecture" (equation H_i and its PyTorch listing);
+// top-s candidates per head: same page, tree-attention section.
+//
+// Decoding with a batch of B <= 16 sequences streams K*(d*d + V*d) weights
+// once per step, so both stages are HBM-bound weight streams.  Each weight
+// tile of 16 output rows is the A operand of a 16x16 MFMA whose B operand is
+// the (at most 16) batch columns, so one kernel serves every B <= 16 and the
+// FLOPs cost nothing next to the bytes.
+//
+// Stage 1: grid of 16-row tiles over the K*d rows of W1, four waves per tile
+//   splitting the d reduction; LDS sum; epilogue z = SiLU(u) + h written to
+//   the workspace (bf16 rounding once, in bf16 mode).  Also clears the
+//   per-head arrival counters used by stage 2.
+// Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over P
+//   workgroups (P waves of work per CU pair); each wave streams its tiles
+//   with several 16-byte loads in flight, keeps a per-lane top-s list of its
+//   column, merges lists across lanes (shuffles) and waves (LDS), and writes
+//   one partial list per (head, sequence) for its workgroup.  The last
+//   workgroup to finish a head (device-scope counter) merges that head's
+//   partial lists into topk_ids / topk_vals.
+#include "common.h"
+
+namespace medusa {
+namespace {
+
+constexpr int kSMax = MEDUSA_MAX_TOPS;   // top-s list capacity
+constexpr int kS1Waves = 4;              // stage 1: waves per 16-row tile (split d)
+constexpr int kS1Unroll = 8;             // stage 1: k-steps in flight per wave
+constexpr int kS2Waves = 8;              // stage 2: waves per workgroup
+constexpr int kS2Tiles = 4;              // stage 2: row tiles per wave pass
+constexpr int kS2Unroll = 4;             // stage 2: k-steps in flight per wave
+constexpr int kS2MaxWG = kNumCU;         // stage 2: workgroups (one per CU)
+
+struct HeadsLayout {
+    size_t z_off, cnt_off, part_off, total;
+    int ntph, nt, P;
+};
+
+inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
+
+inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype) {
+    HeadsLayout L;
+    L.ntph = (V + 15) / 16;
+    L.nt = K * L.ntph;
+    L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
+    L.z_off = 0;
+    L.cnt_off = align_up((size_t)B * K * d * esize(dtype), 256);
+    L.part_off = L.cnt_off + align_up((size_t)K * sizeof(uint32_t), 256);
+    L.total = L.part_off + align_up((size_t)K * B * L.P * kSMax * 2 * sizeof(float), 256);
+    return L;
+}
+
+// ------------------------------------------------------------------ stage 1
+template <typename T>
+__global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
+    const T *__restrict__ hidden, const T *__restrict__ w1, T *__restrict__ z,
+    uint32_t *__restrict__ counters, int B, int K, int d) {
+    constexpr int KC = Elem<T>::kPer16B;  // elements per lane per k-step
+    constexpr int KSTEP = 4 * KC;         // k per step (4 lane groups)
+    __shared__ f32x4 red[kS1Waves][kWave];
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int g = lane / 16, c = lane % 16;
+    const int tile = blockIdx.x;                 // 16 rows of the K*d row space
+    const int head = (tile * 16) / d;
+    const int row0 = tile * 16 - head * d;      // first row within the head
+    if (blockIdx.x == 0 && threadIdx.x < K) counters[threadIdx.x] = 0u;
+
+    const int kspan = d / kS1Waves;
+    const int kbeg = wave * kspan;
+    const T *arow = w1 + ((size_t)head * d + row0 + c) * (size_t)d + kbeg + g * KC;
+    const bool bcol = c < B;
+    const T *brow = hidden + (size_t)(bcol ? c : 0) * d + kbeg + g * KC;
+
+    // kspan = d/4 is a multiple of KSTEP (d % 128 == 0); the unrolled body
+    // covers whole groups of kS1Unroll steps, the tail loop the rest.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int k0 = 0;
+    for (; k0 + KSTEP * kS1Unroll <= kspan; k0 += KSTEP * kS1Unroll) {
+        u32x4 a[kS1Unroll], b[kS1Unroll];
+#pragma unroll
+        for (int u = 0; u < kS1Unroll; ++u) {
+            a[u] = ld16(arow + k0 + u * KSTEP);
+            b[u] = bcol ? ld16(brow + k0 + u * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kS1Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
+    }
+    for (; k0 < kspan; k0 += KSTEP) {
+        const u32x4 a = ld16(arow + k0);
+        const u32x4 b = bcol ? ld16(brow + k0) : u32x4{0u, 0u, 0u, 0u};
+        mma16_step(acc, a, b, T{});
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 u = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kS1Waves; ++w) u += red[w][lane];
+    if (!bcol) return;
+    // lane holds rows row0 + 4g + i of column (sequence) c
+    const T *hrow = hidden + (size_t)c * d;
+    T *zrow = z + ((size_t)c * K + head) * d + row0 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = row0 + 4 * g + i;
+        const float x = u[i];
+        const float silu = x / (1.0f + expf(-x));
+        zrow[i] = Elem<T>::from_f32(silu + Elem<T>::to_f32(hrow[j]));
+    }
+}
+
+// ------------------------------------------------------------- top-s lists
+struct TopList {
+    float v[kSMax];
+    int id[kSMax];
+    __device__ void clear() {
+#pragma unroll
+        for (int r = 0; r < kSMax; ++r) {
+            v[r] = -INFINITY;
+            id[r] = 0x7FFFFFFF;
+        }
+    }
+    // the s-th entry (the admission bar), read without dynamic indexing
+    __device__ void bar(int s, float &bv, int &bi) const {
+        bv = v[0];
+        bi = id[0];
+#pragma unroll
+        for (int r = 1; r < kSMax; ++r)
+            if (r == s - 1) {
+                bv = v[r];
+                bi = id[r];
+            }
+    }
+    // insert keeping the first s entries sorted; entries past s stay sentinels
+    __device__ void insert(float x, int i, int s) {
+        float bv;
+        int bi;
+        bar(s, bv, bi);
+        if (!cand_before(x, i, bv, bi)) return;
+#pragma unroll
+        for (int r = kSMax - 1; r >= 0; --r) {
+            if (r >= s) continue;
+            const bool here_better = cand_before(x, i, v[r], id[r]);
+            const bool above_better = r == 0 || cand_before(x, i, v[r > 0 ? r - 1 : 0], id[r > 0 ? r - 1 : 0]);
+            if (here_better) {
+                if (above_better && r > 0) {  // x moves further up: shift entry r-1 down
+                    v[r] = v[r - 1];
+                    id[r] = id[r - 1];
+                } else {                      // x lands here
+                    v[r] = x;
+                    id[r] = i;
+                }
+            }
+        }
+    }
+    __device__ void pop() {
+#pragma unroll
+        for (int r = 0; r < kSMax - 1; ++r) {
+            v[r] = v[r + 1];
+            id[r] = id[r + 1];
+        }
+        v[kSMax - 1] = -INFINITY;
+        id[kSMax - 1] = 0x7FFFFFFF;
+    }
+};
+
+// Merge the sorted lists held by the lanes {lane ^ m : m = m0, 2*m0, ..., 32}
+// (m0 = 16: the four lanes sharing a 16x16 tile column; m0 = 1: the whole
+// wave).  Afterwards every lane of a group holds in ov/oi the best s of the
+// union of its group's lists.  Lists are consumed.  Ids within a group are
+// distinct.
+__device__ void group_merge(TopList &L, int s, int m0, float (&ov)[kSMax], int (&oi)[kSMax]) {
+#pragma unroll
+    for (int r = 0; r < kSMax; ++r) {
+        ov[r] = -INFINITY;
+        oi[r] = 0x7FFFFFFF;
+        if (r >= s) continue;
+        float bv = L.v[0];
+        int bi = L.id[0];
+        for (int m = m0; m < kWave; m <<= 1) {
+            const float v2 = __shfl_xor(bv, m);
+            const int i2 = __shfl_xor(bi, m);
+            if (cand_before(v2, i2, bv, bi)) {
+                bv = v2;
+                bi = i2;
+            }
+        }
+        ov[r] = bv;
+        oi[r] = bi;
+        if (L.id[0] == bi && L.v[0] == bv) L.pop();
+    }
+}
+
+// ------------------------------------------------------------------ stage 2
+template <typename T>
+__global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
+    const T *__restrict__ w2, const T *__restrict__ z, float *__restrict__ logits_out,
+    int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals, uint32_t *__restrict__ counters,
+    float2 *__restrict__ part, int B, int K, int d, int V, int s, int ntph, int nt, int P) {
+    constexpr int KC = Elem<T>::kPer16B;
+    constexpr int KSTEP = 4 * KC;
+    // per-wave merged lists: [wave][head slot 0/1][column][s]
+    __shared__ float2 stage[kS2Waves][2][16][kSMax];
+    __shared__ int merge_head[2];
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int g = lane / 16, c = lane % 16;
+    const int wg = blockIdx.x;
+
+    for (int i = threadIdx.x; i < kS2Waves * 2 * 16 * kSMax; i += blockDim.x)
+        (&stage[0][0][0][0])[i] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
+    if (threadIdx.x < 2) merge_head[threadIdx.x] = -1;
+
+    const long long wg_beg = (long long)wg * nt / P, wg_end = (long long)(wg + 1) * nt / P;
+    const int head_lo = (int)(wg_beg / ntph);
+    const long long span = wg_end - wg_beg;
+    long long tile = wg_beg + span * wave / kS2Waves;
+    const long long wend = wg_beg + span * (wave + 1) / kS2Waves;
+    __syncthreads();
+
+    const bool bcol = c < B;
+    TopList L;
+    L.clear();
+    int cur_head = tile < wend ? (int)(tile / ntph) : -1;
+
+    while (tile < wend) {
+        const int head = (int)(tile / ntph);
+        if (head != cur_head) {
+            // flush the finished head's lists
+            float ov[kSMax];
+            int oi[kSMax];
+            group_merge(L, s, 16, ov, oi);
+            if (g == 0) {
+#pragma unroll
+                for (int r = 0; r < kSMax; ++r)
+                    if (r < s)
+                        stage[wave][cur_head - head_lo][c][r] = make_float2(ov[r], __int_as_float(oi[r]));
+            }
+            L.clear();
+            cur_head = head;
+        }
+        const long long head_end = (long long)(head + 1) * ntph;
+        const long long gend = tile + kS2Tiles < wend ? tile + kS2Tiles : wend;
+        const int n = (int)((gend < head_end ? gend : head_end) - tile);
+        const int tile_in_head = (int)(tile - (long long)head * ntph);
+
+        const T *arow[kS2Tiles];
+#pragma unroll
+        for (int r = 0; r < kS2Tiles; ++r) {
+            int row = (tile_in_head + r) * 16 + c;
+            row = row < V ? row : V - 1;
+            arow[r] = w2 + ((size_t)head * V + row) * (size_t)d + g * KC;
+        }
+        const T *brow = z + ((size_t)(bcol ? c : 0) * K + head) * d + g * KC;
+
+        f32x4 acc[kS2Tiles];
+#pragma unroll
+        for (int r = 0; r < kS2Tiles; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int k0 = 0; k0 < d; k0 += KSTEP * kS2Unroll) {
+            u32x4 a[kS2Tiles][kS2Unroll], b[kS2Unroll];
+#pragma unroll
+            for (int u = 0; u < kS2Unroll; ++u)
+                b[u] = bcol ? ld16(brow + k0 + u * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int r = 0; r < kS2Tiles; ++r)
+                if (r < n) {
+#pragma unroll
+                    for (int u = 0; u < kS2Unroll; ++u) a[r][u] = ld16(arow[r] + k0 + u * KSTEP);
+                }
+#pragma unroll
+            for (int u = 0; u < kS2Unroll; ++u)
+#pragma unroll
+                for (int r = 0; r < kS2Tiles; ++r)
+                    if (r < n) mma16_step(acc[r], a[r][u], b[u], T{});
+        }
+
+        // epilogue: lane holds rows 16*tile + 4g + i of column c
+#pragma unroll
+        for (int r = 0; r < kS2Tiles; ++r) {
+            if (r >= n) continue;
+            const int v0 = (tile_in_head + r) * 16 + 4 * g;
+            if (bcol) {
+                if (logits_out) {
+                    float *dst = logits_out + ((size_t)c * K + head) * V + v0;
+                    if (v0 + 3 < V && ((V & 3) == 0)) {
+                        *reinterpret_cast<f32x4 *>(dst) = acc[r];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (v0 + i < V) dst[i] = acc[r][i];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v0 + i < V) L.insert(acc[r][i], v0 + i, s);
+            }
+        }
+        tile += n;
+    }
+    if (cur_head >= 0) {
+        float ov[kSMax];
+        int oi[kSMax];
+        group_merge(L, s, 16, ov, oi);
+        if (g == 0) {
+#pragma unroll
+            for (int r = 0; r < kSMax; ++r)
+                if (r < s)
+                    stage[wave][cur_head - head_lo][c][r] = make_float2(ov[r], __int_as_float(oi[r]));
+        }
+    }
+    __syncthreads();
+
+    // workgroup merge: one thread per (head slot, column)
+    const int head_hi = (int)((wg_end - 1) / ntph);
+    const int nslot = head_hi - head_lo + 1;
+    if (threadIdx.x < nslot * 16) {
+        const int slot = threadIdx.x / 16, col = threadIdx.x % 16;
+        const int head = head_lo + slot;
+        if (col < B) {
+            // first workgroup that owns a tile of this head
+            const long long first_tile = (long long)head * ntph;
+            const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
+            float2 *dst = part + (((size_t)head * B + col) * P + (wg - wg_first)) * kSMax;
+            for (int r = 0; r < s; ++r) {
+                float bv = -INFINITY;
+                int bi = 0x7FFFFFFF, bw = -1, br = -1;
+                for (int w = 0; w < kS2Waves; ++w)
+                    for (int q = 0; q < s; ++q) {
+                        const float2 e = stage[w][slot][col][q];
+                        const int id = __float_as_int(e.y);
+                        if (id == 0x7FFFFFFF) continue;
+                        if (cand_before(e.x, id, bv, bi)) {
+                            bv = e.x;
+                            bi = id;
+                            bw = w;
+                            br = q;
+                        }
+                    }
+                if (bw >= 0) stage[bw][slot][col][br] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
+                dst[r] = make_float2(bv, __int_as_float(bi));
+            }
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x < nslot) {
+        const int head = head_lo + threadIdx.x;
+        const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
+        const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
+        const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
+        const uint32_t need = (uint32_t)(wg_last - wg_first + 1);
+        const uint32_t old = atomicAdd(&counters[head], 1u);
+        merge_head[threadIdx.x] = (old + 1 == need) ? head : -1;
+    }
+    __syncthreads();
+
+    // the last workgroup of a head merges its partial lists: one wave per column
+    for (int slot = 0; slot < nslot; ++slot) {
+        const int head = merge_head[slot];
+        if (head < 0) continue;
+        __threadfence();
+        const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
+        const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
+        const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
+        const int nparts = wg_last - wg_first + 1;
+        for (int col = wave; col < B; col += kS2Waves) {
+            TopList M;
+            M.clear();
+            const float2 *src = part + ((size_t)head * B + col) * P * kSMax;
+            for (int p = lane; p < nparts; p += kWave)
+#pragma unroll
+                for (int r = 0; r < kSMax; ++r) {
+                    if (r >= s) continue;
+                    const float2 e = src[(size_t)p * kSMax + r];
+                    const int id = __float_as_int(e.y);
+                    if (id != 0x7FFFFFFF) M.insert(e.x, id, s);
+                }
+            float ov[kSMax];
+            int oi[kSMax];
+            group_merge(M, s, 1, ov, oi);
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < kSMax; ++r) {
+                    if (r >= s) continue;
+                    topk_ids[((size_t)col * K + head) * s + r] = oi[r];
+                    if (topk_vals) topk_vals[((size_t)col * K + head) * s + r] = ov[r];
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- host side
+int check_heads_args(const void *w, int B, int K, int d, int V, int s, int dtype) {
+    if (!w) return MEDUSA_ERR_NULL;
+    if (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16) return MEDUSA_ERR_DTYPE;
+    if (B < 1 || B > MEDUSA_MAX_BATCH || K < 1 || K > MEDUSA_MAX_HEADS || d < 128 || d > 16384 ||
+        d % 128 != 0 || V < 1 || s < 1 || s > MEDUSA_MAX_TOPS || s > V)
+        return MEDUSA_ERR_SHAPE;
+    if ((long long)K * V * d >= (1LL << 62)) return MEDUSA_ERR_SHAPE;
+    return MEDUSA_OK;
+}
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (!ws) return MEDUSA_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return MEDUSA_ERR_WORKSPACE;
+    if (ws_bytes < need) return MEDUSA_ERR_WORKSPACE;
+    return MEDUSA_OK;
+}
+
+int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V, int dtype,
+                  void *ws, hipStream_t st) {
+    const HeadsLayout L = heads_layout(B, K, d, V, dtype);
+    char *base = (char *)ws;
+    uint32_t *cnt = (uint32_t *)(base + L.cnt_off);
+    const dim3 grid((unsigned)((size_t)K * d / 16)), block(kS1Waves * kWave);
+    if (dtype == MEDUSA_BF16)
+        hipLaunchKernelGGL(heads_stage1_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)hidden,
+                           (const bf16_t *)w1, (bf16_t *)(base + L.z_off), cnt, B, K, d);
+    else
+        hipLaunchKernelGGL(heads_stage1_kernel<float>, grid, block, 0, st, (const float *)hidden,
+                           (const float *)w1, (float *)(base + L.z_off), cnt, B, K, d);
+    return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+int launch_stage2(const void *w2, int B, int K, int d, int V, int s, int dtype, float *logits_out,
+                  int32_t *topk_ids, float *topk_vals, void *ws, hipStream_t st) {
+    const HeadsLayout L = heads_layout(B, K, d, V, dtype);
+    char *base = (char *)ws;
+    uint32_t *cnt = (uint32_t *)(base + L.cnt_off);
+    float2 *part = (float2 *)(base + L.part_off);
+    const dim3 grid((unsigned)L.P), block(kS2Waves * kWave);
+    if (dtype == MEDUSA_BF16)
+        hipLaunchKernelGGL(heads_stage2_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)w2,
+                           (const bf16_t *)(base + L.z_off), logits_out, topk_ids, topk_vals, cnt,
+                           part, B, K, d, V, s, L.ntph, L.nt, L.P);
+    else
+        hipLaunchKernelGGL(heads_stage2_kernel<float>, grid, block, 0, st, (const float *)w2,
+                           (const float *)(base + L.z_off), logits_out, topk_ids, topk_vals, cnt,
+                           part, B, K, d, V, s, L.ntph, L.nt, L.P);
+    return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace medusa
+
+using namespace medusa;
+
+extern "C" size_t medusa_heads_topk_workspace_bytes(int B, int K, int d, int V, int s, int dtype) {
+    if (check_heads_args((const void *)1, B, K, d, V, s, dtype) != MEDUSA_OK) return 0;
+    return heads_layout(B, K, d, V, dtype).total;
+}
+
+extern "C" int medusa_heads_stage1(const void *hidden, const void *w1, int B, int K, int d, int V,
+                                   int s, int dtype, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_heads_args(w1, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!hidden) return MEDUSA_ERR_NULL;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage1(hidden, w1, B, K, d, V, dtype, ws, (hipStream_t)stream);
+}
+
+extern "C" int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, int s, int dtype,
+                                   float *logits_out, int32_t *topk_ids, float *topk_vals,
+                                   void *ws, size_t ws_bytes, void *stream) {
+    int st = check_heads_args(w2, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!topk_ids) return MEDUSA_ERR_NULL;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2(w2, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals, ws,
+                         (hipStream_t)stream);
+}
+
+extern "C" int medusa_heads_topk(const void *hidden, const void *w1, const void *w2, int B, int K,
+                                 int d, int V, int s, int dtype, float *logits_out,
+                                 int32_t *topk_ids, float *topk_vals, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    int st = check_heads_args(w2, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!hidden || !w1 || !topk_ids) return MEDUSA_ERR_NULL;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    st = launch_stage1(hidden, w1, B, K, d, V, dtype, ws, (hipStream_t)stream);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2(w2, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals, ws,
+                         (hipStream_t)stream);
+}

@@ -1,0 +1,488 @@
+// Tree attention on gfx950: every candidate-tree node attends to the whole
+// KV-cache prefix of its sequence plus its own tree ancestors and itself, in
+// one pass (paper explainer page, tree-attention section: the ancestor mask
+// lets all candidate paths be verified in a single forward pass without
+// growing the batch).
+//
+// Work decomposition.  For a (sequence b, kv head) pair, the G = Hq/Hkv
+// query heads that share it and the T tree nodes form M = G*T query rows that
+// all read the same keys, so they are packed as the N dimension of one MFMA
+// problem and share every K/V tile staged in LDS.  A workgroup of W <= 8
+// waves owns 32*W rows (an "m-tile") and one slice ("split") of the prefix;
+// the split holding the end of the prefix also takes the T tree keys, with
+// the ancestor-or-self mask applied from per-row bitmasks that each lane
+// builds from the parent array (kernel argument).  Splits are merged by a
+// log-sum-exp combine kernel.  Block ids are remapped so that the m-tiles and
+// splits of one (b, kv head) run on the same XCD and share its L2.
+//
+// Per wave and 32-key sub-block (S^T = K Q^T, then O^T += V^T P^T):
+//   - S^T on 32x32 MFMAs: A = K rows (keys) from LDS, B = Q^T from registers
+//     (each lane owns one query column);
+//   - online softmax per lane in the log2 domain (scores * scale * log2 e),
+//     the running max shared with the partner lane (lane ^ 32);
+//   - P^T goes straight from the S^T accumulators into the B operand, V^T
+//     comes from LDS, where V is stored transposed (and, for bf16, with its
+//     4-key groups reordered so each lane reads one 16-byte chunk).
+#include "common.h"
+
+namespace medusa {
+namespace {
+
+constexpr int kBN = 64;          // keys per LDS stage
+constexpr int kMaxWaves = 8;     // waves per workgroup
+constexpr int kMinChunk = 256;   // smallest prefix split (keys)
+constexpr int kTargetWG = 2 * kNumCU;
+
+template <typename T, int DH>
+struct Cfg {
+    static constexpr int KC = Elem<T>::kPer16B;      // elements per 16-byte chunk
+    static constexpr int KSTEP = 2 * KC;              // dh per MFMA k-step
+    static constexpr int NKS = DH / KSTEP;            // k-steps for q.k
+    static constexpr int NDT = DH / 32;               // 32-row dh tiles of O^T
+    static constexpr int CPR = DH / KC;               // 16-byte chunks per K row
+    static constexpr int KS_STRIDE = DH * (int)sizeof(T) + 16;   // bytes per key row
+    static constexpr int VT_STRIDE = kBN * (int)sizeof(T) + 16;  // bytes per dh row
+    static constexpr int KS_BYTES = kBN * KS_STRIDE;
+    static constexpr int VT_BYTES = DH * VT_STRIDE;
+    static constexpr int LDS_BYTES = KS_BYTES + VT_BYTES;
+};
+
+struct AttnParams {
+    const void *q, *kc, *vc, *kt, *vt;
+    const int32_t *prefix_len;
+    void *out;
+    uint64_t *mask_out;
+    float *part_o;      // [nsplit][B][Hq][T][dh]
+    float2 *part_ml;    // [nsplit][B][Hq][T]  (max in log2 units, sum)
+    int32_t *err;
+    int B, Hq, Hkv, Lcap, T, G, M, W, nmt, nsplit, chunk, nwg;
+    float c;            // scale * log2(e)
+    uint8_t parent[MEDUSA_MAX_TREE];   // parent index; 255 marks the root (never a parent: parent < n <= 255)
+};
+
+// position of key k (0..63) of a stage inside a transposed V row
+template <typename T>
+__device__ __forceinline__ int vt_pos(int k);
+template <>
+__device__ __forceinline__ int vt_pos<float>(int k) { return k; }
+template <>
+__device__ __forceinline__ int vt_pos<bf16_t>(int k) {
+    // within each 16 keys, 4-key group a goes to 8*(a%2) + 4*(a/2)
+    const int a = (k >> 2) & 3;
+    return (k & ~15) + 8 * (a & 1) + 4 * (a >> 1) + (k & 3);
+}
+
+// Stage keys [k0, k0 + nvalid) of one (b, kv head) into LDS: K as rows, V
+// transposed.  Rows past nvalid are zero (their scores are masked; zero V
+// keeps 0 * garbage out of the sums).
+template <typename T, int DH>
+__device__ __forceinline__ void stage_block(char *lds, const T *__restrict__ kb,
+                                            const T *__restrict__ vb, int nvalid, int tid,
+                                            int nthr) {
+    using C = Cfg<T, DH>;
+    char *Ks = lds;
+    char *Vt = lds + C::KS_BYTES;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int ch = tid; ch < kBN * C::CPR; ch += nthr) {
+        const int key = ch / C::CPR, col = ch % C::CPR;
+        const u32x4 v = key < nvalid ? ld16(kb + (size_t)key * DH + col * C::KC) : zero;
+        st16(Ks + key * C::KS_STRIDE + col * 16, v);
+    }
+    // V: a unit is 4 consecutive keys x one 16-byte column chunk
+    for (int u = tid; u < (kBN / 4) * C::CPR; u += nthr) {
+        const int col = u % C::CPR, kg = u / C::CPR;
+        u32x4 r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = 4 * kg + j;
+            r[j] = key < nvalid ? ld16(vb + (size_t)key * DH + col * C::KC) : zero;
+        }
+        const int pos = vt_pos<T>(4 * kg);
+#pragma unroll
+        for (int e = 0; e < C::KC; ++e) {
+            char *dst = Vt + (col * C::KC + e) * C::VT_STRIDE + pos * (int)sizeof(T);
+            if constexpr (sizeof(T) == 2) {
+                const int w = e >> 1, sh = (e & 1) * 16;
+                const uint32_t lo = ((r[0][w] >> sh) & 0xFFFFu) | (((r[1][w] >> sh) & 0xFFFFu) << 16);
+                const uint32_t hi = ((r[2][w] >> sh) & 0xFFFFu) | (((r[3][w] >> sh) & 0xFFFFu) << 16);
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{lo, hi};
+            } else {
+                st16(dst, u32x4{r[0][e], r[1][e], r[2][e], r[3][e]});
+            }
+        }
+    }
+}
+
+struct RowState {
+    float m;      // running max of scores * c (log2 units), shared by lane pair
+    float l;      // this lane's part of the softmax denominator
+};
+
+// One 64-key stage for one wave: two 32-key sub-blocks.
+// kind 0: prefix keys, valid while key < klim; kind 1: tree keys, valid where
+// the row's ancestor bit is set (mword = mask word of keys [tb, tb+64)).
+template <typename T, int DH>
+__device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[Cfg<T, DH>::NKS],
+                                             f32x16 (&o)[Cfg<T, DH>::NDT], RowState &st, int lane,
+                                             int kind, int klim, uint64_t mword, float c) {
+    using C = Cfg<T, DH>;
+    const char *Ks = lds;
+    const char *Vt = lds + C::KS_BYTES;
+    const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        f32x16 s = {};
+        const char *krow = Ks + (sub * 32 + col) * C::KS_STRIDE + h * 16;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(krow + ks * 32);
+            mma32_step(s, a, qf[ks], T{});
+        }
+        // s[4i+j] = score of key sub*32 + 8i + 4h + j for this lane's query
+        float x[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool ok = kind == 0 ? key < klim : ((mword >> key) & 1ull) != 0ull;
+            x[r] = ok ? s[r] * c : -INFINITY;
+            mx = fmaxf(mx, x[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(st.m - mref);
+        float p[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = exp2f(x[r] - mref);
+            psum += p[r];
+        }
+        st.l = st.l * alpha + psum;
+        st.m = mnew;
+        if (alpha != 1.0f) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+        }
+        // O^T[dh][q] += V^T[dh][key] P^T[key][q]
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const char *vrow = Vt + (dt * 32 + col) * C::VT_STRIDE;
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                        vrow + (sub * 32 + 16 * mm + 8 * h) * 2);
+                    u32x4 b;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        b[w] = (uint32_t)f32_to_bf16(p[8 * mm + 2 * w]) |
+                               ((uint32_t)f32_to_bf16(p[8 * mm + 2 * w + 1]) << 16);
+                    mma32_step(o[dt], a, b, T{});
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                        vrow + (sub * 32 + 8 * i + 4 * h) * 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mma32_f32_single(o[dt], __uint_as_float(a[j]), p[4 * i + j]);
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(kMaxWaves *kWave) void tree_attn_fwd_kernel(AttnParams p) {
+    using C = Cfg<T, DH>;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ uint8_t par[MEDUSA_MAX_TREE];
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    for (int i = tid; i < p.T; i += nthr) par[i] = p.parent[i];
+
+    // logical block -> (b, kv head, split, m-tile), m-tile fastest
+    const uint32_t lid = xcd_logical_id(blockIdx.x, (uint32_t)p.nwg);
+    const int mt = (int)(lid % p.nmt);
+    const int split = (int)((lid / p.nmt) % p.nsplit);
+    const int kvh = (int)((lid / ((uint32_t)p.nmt * p.nsplit)) % p.Hkv);
+    const int b = (int)(lid / ((uint32_t)p.nmt * p.nsplit * p.Hkv));
+
+    if (lid == 0 && tid == 0) {
+        int bad = 0;
+        for (int i = 0; i < p.B; ++i) bad |= (p.prefix_len[i] < 0 || p.prefix_len[i] > p.Lcap);
+        *p.err = bad;
+    }
+    int L = p.prefix_len[b];
+    L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+    const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+    __syncthreads();
+    if (p.mask_out && lid == 0) {
+        const int W = (p.T + 63) / 64;
+        for (int n = tid; n < p.T; n += nthr) {
+            uint64_t w[4] = {0ull, 0ull, 0ull, 0ull};
+            // walk n, parent(n), ..., root (whose parent entry is 255)
+            for (int a = n, guard = 0; guard <= p.T; a = par[a], ++guard) {
+                w[a >> 6] |= 1ull << (a & 63);
+                if (par[a] == 255) break;
+            }
+            for (int k = 0; k < W; ++k) p.mask_out[(size_t)n * W + k] = w[k];
+        }
+    }
+    if (split >= nsb) return;
+    const int kbeg = split * p.chunk;
+    const int kend = kbeg + p.chunk < L ? kbeg + p.chunk : L;
+    const bool last = split == nsb - 1;
+
+    // this lane's query row
+    const int col = lane & 31, h = lane >> 5;
+    const int row = mt * 32 * p.W + wave * 32 + col;
+    const bool rvalid = row < p.M;
+    const int g = rvalid ? row / p.T : 0;
+    const int t = rvalid ? row % p.T : 0;
+    const int hq = kvh * p.G + g;
+
+    u32x4 qf[C::NKS];
+    {
+        const T *qrow = (const T *)p.q + (((size_t)b * p.Hq + hq) * p.T + t) * DH;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+            qf[ks] = rvalid ? ld16(qrow + ks * C::KSTEP + h * C::KC) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
+    for (int a = t, guard = 0; guard <= p.T; a = par[a], ++guard) {
+        const uint64_t bit = 1ull << (a & 63);
+        const int wi = a >> 6;
+        mw0 |= wi == 0 ? bit : 0ull;
+        mw1 |= wi == 1 ? bit : 0ull;
+        mw2 |= wi == 2 ? bit : 0ull;
+        mw3 |= wi == 3 ? bit : 0ull;
+        if (par[a] == 255) break;   // a is the root
+    }
+
+    f32x16 o[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{};
+    RowState st{-INFINITY, 0.f};
+
+    const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
+    for (int k0 = kbeg; k0 < kend; k0 += kBN) {
+        const int nv = kend - k0 < kBN ? kend - k0 : kBN;
+        __syncthreads();
+        stage_block<T, DH>(lds, (const T *)p.kc + kvbase + (size_t)k0 * DH,
+                           (const T *)p.vc + kvbase + (size_t)k0 * DH, nv, tid, nthr);
+        __syncthreads();
+        attend_stage<T, DH>(lds, qf, o, st, lane, 0, nv, 0ull, p.c);
+    }
+    if (last) {
+        const size_t tbase = ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
+        for (int tb = 0; tb < p.T; tb += kBN) {
+            const int nv = p.T - tb < kBN ? p.T - tb : kBN;
+            __syncthreads();
+            stage_block<T, DH>(lds, (const T *)p.kt + tbase + (size_t)tb * DH,
+                               (const T *)p.vt + tbase + (size_t)tb * DH, nv, tid, nthr);
+            __syncthreads();
+            const int wi = tb >> 6;
+            const uint64_t mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+            attend_stage<T, DH>(lds, qf, o, st, lane, 1, 0, mword, p.c);
+        }
+    }
+
+    const float ltot = st.l + __shfl_xor(st.l, 32);
+    if (!rvalid) return;
+    const size_t orow = ((size_t)b * p.Hq + hq) * p.T + t;
+    if (nsb == 1) {
+        const float inv = 1.0f / ltot;
+        T *dst = (T *)p.out + orow * DH;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                T *d4 = dst + dt * 32 + 8 * i + 4 * h;
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t lo = (uint32_t)f32_to_bf16(o[dt][4 * i] * inv) |
+                                        ((uint32_t)f32_to_bf16(o[dt][4 * i + 1] * inv) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(o[dt][4 * i + 2] * inv) |
+                                        ((uint32_t)f32_to_bf16(o[dt][4 * i + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2 *>(d4) = u32x2{lo, hi};
+                } else {
+                    *reinterpret_cast<f32x4 *>(d4) =
+                        f32x4{o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
+                              o[dt][4 * i + 3] * inv};
+                }
+            }
+    } else {
+        const size_t prow = (size_t)split * p.B * p.Hq * p.T + orow;
+        float *dst = p.part_o + prow * DH;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4 *>(dst + dt * 32 + 8 * i + 4 * h) =
+                    f32x4{o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]};
+        if (h == 0) p.part_ml[prow] = make_float2(st.m, ltot);
+    }
+}
+
+// Merge split partials of the rows whose prefix used more than one split.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
+    const int lane = threadIdx.x % kWave;
+    const size_t rowid = (size_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const size_t nrows = (size_t)p.B * p.Hq * p.T;
+    if (rowid >= nrows) return;
+    const int b = (int)(rowid / ((size_t)p.Hq * p.T));
+    int L = p.prefix_len[b];
+    L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+    const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+    if (nsb == 1) return;
+    float mmax = -INFINITY;
+    for (int sp = 0; sp < nsb; ++sp) mmax = fmaxf(mmax, p.part_ml[(size_t)sp * nrows + rowid].x);
+    constexpr int PER = DH / kWave;
+    float acc[PER] = {};
+    float den = 0.f;
+    for (int sp = 0; sp < nsb; ++sp) {
+        const float2 ml = p.part_ml[(size_t)sp * nrows + rowid];
+        const float w = exp2f(ml.x - mmax);
+        den += w * ml.y;
+        const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * src[lane * PER + e];
+    }
+    const float inv = 1.0f / den;
+    T *dst = (T *)p.out + rowid * DH;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[lane * PER + e] = Elem<T>::from_f32(acc[e] * inv);
+}
+
+struct AttnPlan {
+    int G, M, W, nmt, nsplit, chunk, nwg;
+    size_t err_off, o_off, ml_off, total;
+};
+
+AttnPlan attn_plan(int B, int Hq, int Hkv, int Lcap, int dh, int T, int dtype) {
+    AttnPlan P;
+    P.G = Hq / Hkv;
+    P.M = P.G * T;
+    const int waves = (P.M + 31) / 32;
+    P.W = waves < kMaxWaves ? waves : kMaxWaves;
+    P.nmt = (P.M + 32 * P.W - 1) / (32 * P.W);
+    const long long base = (long long)B * Hkv * P.nmt;
+    int want = (int)((kTargetWG + base - 1) / base);
+    const int cap = Lcap > 0 ? (Lcap + kMinChunk - 1) / kMinChunk : 1;
+    want = want < 1 ? 1 : (want > cap ? cap : want);
+    if (Lcap <= 0) {
+        P.chunk = kBN;
+        P.nsplit = 1;
+    } else {
+        int ch = (Lcap + want - 1) / want;
+        ch = (ch + kBN - 1) / kBN * kBN;
+        P.chunk = ch;
+        P.nsplit = (Lcap + ch - 1) / ch;
+    }
+    P.nwg = (int)(base * P.nsplit);
+    const size_t rows = (size_t)B * Hq * T;
+    P.err_off = 0;
+    P.o_off = 256;
+    const size_t osz = P.nsplit > 1 ? (size_t)P.nsplit * rows * dh * sizeof(float) : 0;
+    P.ml_off = P.o_off + align_up(osz, 256);
+    const size_t mlsz = P.nsplit > 1 ? (size_t)P.nsplit * rows * sizeof(float2) : 0;
+    P.total = P.ml_off + align_up(mlsz, 256);
+    (void)dtype;
+    return P;
+}
+
+int check_tree(const int32_t *parent, int T) {
+    if (!parent) return MEDUSA_ERR_NULL;
+    if (T < 1 || T > MEDUSA_MAX_TREE) return MEDUSA_ERR_SHAPE;
+    if (parent[0] != -1) return MEDUSA_ERR_TREE;
+    for (int n = 1; n < T; ++n)
+        if (parent[n] < 0 || parent[n] >= n) return MEDUSA_ERR_TREE;
+    return MEDUSA_OK;
+}
+
+int check_attn(const void *q, const void *kc, const void *vc, const int32_t *pl, const void *kt,
+               const void *vt, const int32_t *parent, int B, int Hq, int Hkv, int Lcap, int dh,
+               int T, float scale, int dtype, const void *out) {
+    if (!q || !kc || !vc || !pl || !kt || !vt || !out) return MEDUSA_ERR_NULL;
+    if (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16) return MEDUSA_ERR_DTYPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lcap < 0 || (dh != 64 && dh != 128) ||
+        T < 1 || T > MEDUSA_MAX_TREE)
+        return MEDUSA_ERR_SHAPE;
+    if ((long long)B * Hkv * Lcap * dh >= (1LL << 40)) return MEDUSA_ERR_SHAPE;
+    if (!(scale > 0.f) || scale != scale || scale == INFINITY) return MEDUSA_ERR_PARAM;
+    return check_tree(parent, T);
+}
+
+template <typename T, int DH>
+int launch_attn(const AttnParams &p, hipStream_t st) {
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH>), dim3(p.nwg), dim3(p.W * kWave), 0, st, p);
+    if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
+    if (p.nsplit > 1) {
+        const size_t rows = (size_t)p.B * p.Hq * p.T;
+        hipLaunchKernelGGL((tree_attn_combine_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)),
+                           dim3(256), 0, st, p);
+        if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
+    }
+    return MEDUSA_OK;
+}
+
+}  // namespace
+}  // namespace medusa
+
+using namespace medusa;
+
+extern "C" size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int dh, int T,
+                                                 int dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lcap < 0 || (dh != 64 && dh != 128) ||
+        T < 1 || T > MEDUSA_MAX_TREE || (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16))
+        return 0;
+    return attn_plan(B, Hq, Hkv, Lcap, dh, T, dtype).total;
+}
+
+extern "C" int tree_attention(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *prefix_len, const void *k_tree, const void *v_tree,
+                              const int32_t *parent, int B, int Hq, int Hkv, int Lcap, int dh,
+                              int T, float scale, int dtype, void *out, uint64_t *mask_out,
+                              void *ws, size_t ws_bytes, void *stream) {
+    int st = check_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, parent, B, Hq, Hkv, Lcap,
+                        dh, T, scale, dtype, out);
+    if (st != MEDUSA_OK) return st;
+    const AttnPlan P = attn_plan(B, Hq, Hkv, Lcap, dh, T, dtype);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < P.total) return MEDUSA_ERR_WORKSPACE;
+    AttnParams p;
+    p.q = q;
+    p.kc = k_cache;
+    p.vc = v_cache;
+    p.kt = k_tree;
+    p.vt = v_tree;
+    p.prefix_len = prefix_len;
+    p.out = out;
+    p.mask_out = mask_out;
+    p.err = (int32_t *)((char *)ws + P.err_off);
+    p.part_o = (float *)((char *)ws + P.o_off);
+    p.part_ml = (float2 *)((char *)ws + P.ml_off);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Lcap = Lcap;
+    p.T = T;
+    p.G = P.G;
+    p.M = P.M;
+    p.W = P.W;
+    p.nmt = P.nmt;
+    p.nsplit = P.nsplit;
+    p.chunk = P.chunk;
+    p.nwg = P.nwg;
+    p.c = scale * 1.4426950408889634f;
+    for (int i = 0; i < MEDUSA_MAX_TREE; ++i)
+        p.parent[i] = i < T && parent[i] >= 0 ? (uint8_t)parent[i] : (uint8_t)255;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == MEDUSA_BF16)
+        return dh == 128 ? launch_attn<bf16_t, 128>(p, s) : launch_attn<bf16_t, 64>(p, s);
+    return dh == 128 ? launch_attn<float, 128>(p, s) : launch_attn<float, 64>(p, s);
+}

@@ -1,0 +1,121 @@
+"""The C-ABI library: exported symbols, workspace sizing and host-side
+argument validation (CPU only: every call here fails validation before any
+GPU work is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "medusa_verify.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def mv():
+    from medusa_tree_verification_amd import binding
+    return binding
+
+
+def test_every_declared_symbol_is_exported(mv):
+    names = _declared()
+    assert "medusa_heads_topk" in names and "tree_attention" in names and "tree_accept" in names
+    for n in names:
+        assert hasattr(mv.lib, n), n
+    assert set(names) == set(mv.EXPORTS)
+
+
+def test_status_strings_and_version(mv):
+    assert mv.lib.medusa_abi_version() == 1
+    for code in range(-7, 1):
+        assert mv.status_str(code) and mv.status_str(code) != "unknown status"
+    assert mv.status_str(5) == "unknown status"
+
+
+def test_workspace_sizes(mv):
+    L = mv.lib
+    assert L.medusa_heads_topk_workspace_bytes(1, 4, 4096, 32000, 3, 1) >= 4 * 4096 * 2
+    assert L.medusa_heads_topk_workspace_bytes(17, 4, 4096, 32000, 3, 1) == 0     # B > 16
+    assert L.medusa_heads_topk_workspace_bytes(1, 4, 4000, 32000, 3, 1) == 0      # d % 128
+    assert L.medusa_heads_topk_workspace_bytes(1, 4, 4096, 2, 3, 1) == 0          # s > V
+    assert L.tree_attention_workspace_bytes(1, 32, 32, 2048, 128, 64, 1) > 0
+    assert L.tree_attention_workspace_bytes(1, 32, 5, 2048, 128, 64, 1) == 0      # Hq % Hkv
+    assert L.tree_attention_workspace_bytes(1, 32, 8, 2048, 96, 64, 1) == 0       # dh
+    assert L.tree_attention_workspace_bytes(1, 32, 8, 2048, 128, 257, 1) == 0     # T
+    assert L.tree_accept_workspace_bytes(8, 256, 128256, 5, 3) >= 8 * 256
+
+
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+FAKE_WS = ctypes.c_void_p(0x10000)   # 256-aligned
+
+
+def _i32(xs):
+    arr = (ctypes.c_int32 * len(xs))(*xs)
+    return arr
+
+
+def test_heads_validation(mv):
+    L = mv.lib
+    ok = dict(B=1, K=4, d=4096, V=32000, s=3, dt=1)
+
+    def call(hidden=FAKE, w1=FAKE, w2=FAKE, ids=FAKE, ws=FAKE_WS, wsb=1 << 40, **kw):
+        a = dict(ok, **kw)
+        return L.medusa_heads_topk(hidden, w1, w2, a["B"], a["K"], a["d"], a["V"], a["s"], a["dt"],
+                                   None, ids, None, ws, wsb, None)
+    assert call(hidden=None) == -1
+    assert call(w1=None) == -1
+    assert call(ids=None) == -1
+    assert call(dt=7) == -3
+    assert call(B=0) == -2 and call(B=17) == -2 and call(d=100) == -2 and call(s=9) == -2
+    assert call(K=0) == -2 and call(V=2) == -2
+    assert call(ws=None) == -5
+    assert call(ws=ctypes.c_void_p(0x10010)) == -5
+    assert call(wsb=10) == -5
+    assert L.medusa_heads_stage1(FAKE, None, 1, 4, 4096, 32000, 3, 1, FAKE_WS, 1 << 40, None) == -1
+    assert L.medusa_heads_stage2(FAKE, 1, 4, 4096, 32000, 3, 1, None, None, None, FAKE_WS,
+                                 1 << 40, None) == -1
+
+
+def test_attention_validation(mv):
+    L = mv.lib
+    par = _i32([-1, 0, 0, 1])
+
+    def call(parent=par, T=4, Hq=4, Hkv=2, dh=128, scale=0.1, dt=1, out=FAKE, ws=FAKE_WS,
+             wsb=1 << 40, q=FAKE):
+        return L.tree_attention(q, FAKE, FAKE, FAKE, FAKE, FAKE, parent, 2, Hq, Hkv, 64, dh, T,
+                                scale, dt, out, None, ws, wsb, None)
+    assert call(q=None) == -1 and call(out=None) == -1 and call(parent=None) == -1
+    assert call(Hkv=3) == -2 and call(dh=96) == -2 and call(T=0) == -2 and call(T=300) == -2
+    assert call(dt=2) == -3
+    assert call(scale=0.0) == -6 and call(scale=float("nan")) == -6
+    assert call(parent=_i32([0, 0, 0, 1])) == -4          # root not -1
+    assert call(parent=_i32([-1, 0, 3, 1])) == -4         # parent after child
+    assert call(ws=None) == -5 and call(wsb=0) == -5
+
+
+def test_accept_validation(mv):
+    L = mv.lib
+    par = _i32([-1, 0, 0, 1])
+
+    def call(parent=par, rank=None, T=4, K=2, s=2, mode=0, temp=1.0, eps=0.09, delta=0.6, dt=1,
+             ws=FAKE_WS, wsb=1 << 40, logits=FAKE):
+        return L.tree_accept(logits, FAKE, parent, rank, 2, T, 100, K, s, dt, mode, temp, eps,
+                             delta, FAKE, FAKE, FAKE, None, None, ws, wsb, None)
+    assert call(logits=None) == -1 and call(parent=None) == -1
+    assert call(dt=3) == -3
+    assert call(mode=2) == -6
+    assert call(mode=1, temp=0.0) == -6 and call(mode=1, eps=0.0) == -6
+    assert call(mode=1, delta=-1.0) == -6
+    assert call(mode=0, temp=0.0, wsb=0) == -5               # greedy ignores temperature
+    assert call(K=1) == -4                                    # depth 2 > K
+    assert call(s=1) == -4                                    # second child has rank 1
+    assert call(rank=_i32([0, 1, 1, 0])) == -4                # siblings share a rank
+    assert call(rank=_i32([0, 0, 5, 0])) == -4                # rank >= s
+    assert call(T=257) == -2
+    assert call(ws=None) == -5 and call(wsb=0) == -5

@@ -1,0 +1,140 @@
+"""GPU parity: tree_accept against the CPU oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import oracle
+from medusa_tree_verification_amd import workloads as W
+from tests import brute
+from tests.util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("accept_len", "best_node", "accepted_tokens", "node_tokens", "next_token")
+AMBIGUOUS = 1e-4   # typical decisions with |p/threshold - 1| below this are knife-edge
+
+
+def _gpu(logits, ids, parent, mode, temperature=1.0, node_rank=None, eps=0.09, delta=0.6):
+    from medusa_tree_verification_amd import binding as mv
+    m = mv.GREEDY if mode == "greedy" else mv.TYPICAL
+    out = mv.tree_accept(to_dev(logits), to_dev(ids), parent, m, temperature, eps, delta,
+                         node_rank=node_rank)
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _compare(g, ref, tree_paths=None, mode="typical"):
+    """Exact on every output, unless some typical decision is knife-edge: then
+    the GPU result must be the longest valid path for some resolution of the
+    knife-edge decisions, and everything else must still match."""
+    amb = np.abs(ref["ratio"] - 1.0) < AMBIGUOUS
+    amb[:, 0] = False
+    if mode == "greedy":   # argmax on identical inputs: never knife-edge
+        amb[:] = False
+    for k in ("node_tokens",):
+        np.testing.assert_array_equal(g[k], ref[k])
+    B = g["accept_len"].shape[0]
+    n_amb = 0
+    for b in range(B):
+        if not amb[b].any():
+            for k in KEYS:
+                np.testing.assert_array_equal(g[k][b], ref[k][b], err_msg=f"{k} b={b}")
+            continue
+        n_amb += 1
+        assert tree_paths is not None
+        ok = False
+        idx = np.flatnonzero(amb[b])
+        for mask in range(1 << len(idx)):
+            v = ref["valid"][b].copy()
+            for j, n in enumerate(idx):
+                v[n] = (mask >> j) & 1
+            if brute.accept_by_paths(tree_paths, v) == (g["best_node"][b], g["accept_len"][b]):
+                ok = True
+        assert ok, f"b={b}: GPU path is not a valid resolution"
+    return n_amb
+
+
+def _table(seed, B, K, s, V):
+    return W.candidate_table(seed, B, K, s, V)
+
+
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_accept_workloads(name):
+    wl = W.WORKLOADS[name]
+    t = W.workload_tree(wl)
+    ids = _table(1000 * wl.cid + 12, wl.B, wl.K, wl.s, wl.V)
+    logits = W.verify_logits(wl, t, W.path_tokens(t, ids))
+    ref = oracle.tree_accept(logits, ids, t.parent, wl.dtype, wl.mode, wl.temperature)
+    g = _gpu(logits, ids, t.parent, wl.mode, wl.temperature)
+    n_amb = _compare(g, ref, t.paths, wl.mode)
+    print(f"{name}: mean accept_len {ref['accept_len'].mean():.2f}, knife-edge sequences {n_amb}")
+    assert n_amb == 0
+
+
+@pytest.mark.parametrize("mode", ["greedy", "typical"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 7, 64, 1001, 40000])
+def test_accept_random(mode, dtype, V):
+    rng = np.random.default_rng(V)
+    K, s, B = 4, 3, 3
+    t = W.random_tree(V + 7, 40, K, s)
+    ids = np.stack([np.stack([rng.choice(max(V, s), s, replace=False) % V for _ in range(K)])
+                    for _ in range(B)]).astype(np.int32)
+    raw = rng.standard_normal((B, t.T, V)) * (3.0 if mode == "typical" else 1.0)
+    if mode == "greedy":
+        raw = np.round(raw * 2) / 2  # many exact ties -> lowest id must win
+    tok = W.path_tokens(t, ids)
+    for b in range(B):      # make some candidates the argmax / likely
+        for n in range(1, t.T):
+            if rng.random() < 0.6:
+                raw[b, t.parent[n], tok[b, n]] = raw[b, t.parent[n]].max() + (0 if rng.random() < 0.3 else 0.5)
+    logits = W.encode(raw, dtype)
+    ref = oracle.tree_accept(logits, ids, t.parent, dtype, mode, 0.8)
+    g = _gpu(logits, ids, t.parent, mode, 0.8)
+    _compare(g, ref, t.paths, mode)
+
+
+def test_accept_node_rank_and_trivial_trees():
+    rng = np.random.default_rng(3)
+    V, K, s = 50, 3, 4
+    # explicit ranks in a non-sibling-ordinal order
+    parent = np.array([-1, 0, 0, 1, 1, 2], np.int32)
+    rank = np.array([0, 2, 0, 3, 1, 1], np.int32)
+    ids = np.stack([np.stack([rng.choice(V, s, replace=False) for _ in range(K)])
+                    for _ in range(2)]).astype(np.int32)
+    logits = rng.standard_normal((2, 6, V)).astype(np.float32)
+    for b in range(2):
+        logits[b, 0, ids[b, 0, 2]] = 9.0   # node 1 (rank 2) accepted
+        logits[b, 1, ids[b, 1, 3]] = 9.0   # node 3 (rank 3) accepted
+    ref = oracle.tree_accept(logits, ids, parent, "f32", "greedy", node_rank=rank)
+    g = _gpu(logits, ids, parent, "greedy", node_rank=rank)
+    for k in KEYS:
+        np.testing.assert_array_equal(g[k], ref[k])
+    assert ref["accept_len"].tolist() == [2, 2]
+    # root only
+    p1 = np.array([-1], np.int32)
+    r1 = oracle.tree_accept(logits[:, :1], ids, p1, "f32", "typical")
+    g1 = _gpu(logits[:, :1], ids, p1, "typical")
+    for k in KEYS:
+        np.testing.assert_array_equal(g1[k], r1[k])
+    assert g1["accept_len"].tolist() == [0, 0] and g1["accepted_tokens"].max() == -1
+
+
+def test_accept_typical_hand_cases_on_gpu():
+    import json, os
+    gdir = os.path.join(os.path.dirname(__file__), "golden")
+    gold = json.load(open(os.path.join(gdir, "typical_acceptance_cases.json")))
+    for c in gold["cases"]:
+        p = np.array(c["p"])
+        V = len(p)
+        parent = np.array([-1] + [0] * V, np.int32)
+        ids = np.arange(V, dtype=np.int32).reshape(1, 1, V)
+        L = np.zeros((1, V + 1, V), np.float32)
+        L[0, 0] = np.where(p > 0, np.log(np.maximum(p, 1e-300)), -1e4)
+        # the GPU has no valid-bit output: accepted set = which single-child trees accept
+        acc = []
+        for r in range(V):
+            par1 = np.array([-1, 0], np.int32)
+            ids1 = np.array([[[r]]], np.int32)
+            g = _gpu(L[:, :2], ids1, par1, "typical", 1.0, eps=gold["eps"], delta=gold["delta"])
+            if g["accept_len"][0] == 1:
+                acc.append(r)
+        assert acc == c["accepted"], c["name"]
