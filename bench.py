@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the Medusa verify step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the K Medusa heads
+with top-s (two launches: W1 stage, W2 stage with fused top-s), one tree
+attention pass over the KV prefix and the tree, and tree acceptance.  Inputs
+are seeded synthetic tensors resident in HBM before timing starts.
+
+Prints one JSON line.  Per-call durations come from HIP events recorded on
+the stream the library launches on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from medusa_tree_verification_amd import workloads as W  # noqa: E402
+
+METRIC = "tree-verify steps/s (heads+tree-attn+accept); achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama7b_b1", choices=W.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle timing")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, prefix_len, n_internal):
+    """Bytes each call must move at least once (inputs read + outputs written)."""
+    w = 2 if wl.dtype == W.BF16 else 4
+    B, K, d, V, s, T = wl.B, wl.K, wl.d, wl.V, wl.s, wl.T
+    stage1 = K * d * d * w + B * d * w + B * K * d * w              # W1, h in; z out
+    stage2 = K * V * d * w + B * K * d * w + B * K * s * 8          # W2, z in; ids+vals out
+    Ltot = int(np.minimum(prefix_len, wl.Lcap).sum())
+    attn = (2 * wl.Hkv * Ltot * wl.dh * w + 2 * B * wl.Hkv * T * wl.dh * w
+            + 2 * B * wl.Hq * T * wl.dh * w)                         # KV prefix + tree KV + q in, out
+    accept = B * (n_internal + 1) * V * w                            # internal rows + best row
+    return {"heads_stage1": stage1, "heads_stage2": stage2, "tree_attention": attn,
+            "tree_accept": accept}
+
+
+def attention_flops(wl, prefix_len, tree):
+    depth = np.array([len(p) for p in tree.paths])
+    Ltot = int(np.minimum(prefix_len, wl.Lcap).sum())
+    return 4 * wl.dh * wl.Hq * (wl.T * Ltot + wl.B * int((depth + 1).sum()))
+
+
+def src_digest():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "medusa_tree_verification_amd", "csrc", "heads.hip"), "rb") as f:
+        h.update(f.read())
+    with open(os.path.join(ROOT, "medusa_tree_verification_amd", "csrc", "common.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = src_digest()
+    for line in open(TRAFFIC_FILE):
+        parts = line.split()
+        if len(parts) >= 4 and not line.startswith("#") and parts[0] == workload \
+                and parts[1] == "heads_stage2" and parts[2] == digest:
+            return int(float(parts[3]))
+    return None
+
+
+def calibrate_copy(mib, reps):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "reps": reps}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the verify step shards by sequence, kv head or vocabulary; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, args.steps)
+        return
+    from medusa_tree_verification_amd import binding as mv
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    tree = W.workload_tree(wl)
+
+    def dv(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    hx = W.heads_inputs(wl)
+    ax = W.attention_inputs(wl)
+    hidden, w1, w2 = dv(hx["hidden"]), dv(hx["w1"]), dv(hx["w2"])
+    q, kc, vc, kt, vt = (dv(ax[k]) for k in ("q", "k_cache", "v_cache", "k_tree", "v_tree"))
+    plen = dv(ax["prefix_len"])
+    B, K, d, V, s, T = wl.B, wl.K, wl.d, wl.V, wl.s, wl.T
+    dt = mv.BF16 if wl.dtype == W.BF16 else mv.F32
+    mode = mv.GREEDY if wl.mode == "greedy" else mv.TYPICAL
+
+    ws_h = mv.workspace(mv.lib.medusa_heads_topk_workspace_bytes(B, K, d, V, s, dt), dev)
+    ws_a = mv.workspace(mv.lib.tree_attention_workspace_bytes(B, wl.Hq, wl.Hkv, wl.Lcap, wl.dh, T,
+                                                              dt), dev)
+    ws_c = mv.workspace(mv.lib.tree_accept_workspace_bytes(B, T, V, K, s), dev)
+    ids = torch.empty((B, K, s), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, K, s), dtype=torch.float32, device=dev)
+    attn_out = torch.empty_like(q)
+    i32 = dict(dtype=torch.int32, device=dev)
+    acc = {"accept_len": torch.empty(B, **i32), "best_node": torch.empty(B, **i32),
+           "accepted_tokens": torch.empty((B, K), **i32), "node_tokens": torch.empty((B, T), **i32),
+           "next_token": torch.empty(B, **i32)}
+
+    # verification logits: planted on the candidates the heads actually propose
+    mv.medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws_h)
+    mv.medusa_heads_stage2(w2, B, K, d, V, s, ids, ws_h, topk_vals=vals)
+    torch.cuda.synchronize()
+    cand = ids.cpu().numpy()
+    vlog_np = W.verify_logits(wl, tree, W.path_tokens(tree, cand))
+    vlog = dv(vlog_np)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mv.medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws_h)
+        if ev is not None:
+            ev[1].record()
+        mv.medusa_heads_stage2(w2, B, K, d, V, s, ids, ws_h, topk_vals=vals)
+        if ev is not None:
+            ev[2].record()
+        mv.tree_attention(q, kc, vc, plen, kt, vt, tree.parent, wl.scale, ws=ws_a, out=attn_out)
+        if ev is not None:
+            ev[3].record()
+        mv.tree_accept(vlog, ids, tree.parent, mode, wl.temperature, wl.eps, wl.delta, ws=ws_c,
+                       out=acc)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    names = ["heads_stage1", "heads_stage2", "tree_attention", "tree_accept"]
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in
+           enumerate(names)}
+
+    n_internal = len(set(int(x) for x in tree.parent[1:]))
+    nbytes = algorithmic_bytes(wl, ax["prefix_len"], n_internal)
+    flops = attention_flops(wl, ax["prefix_len"], tree)
+    stages = {n: {"us": round(per[n] * 1e3, 2), "bytes": int(nbytes[n]),
+                  "GBps": round(nbytes[n] / (per[n] * 1e-3) / 1e9, 1)} for n in names}
+    stages["tree_attention"]["TFLOPs"] = round(flops / (per["tree_attention"] * 1e-3) / 1e12, 1)
+    step_bytes = sum(nbytes.values())
+
+    dom = "heads_stage2"
+    achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": K, "hidden": d, "vocab": V,
+                   "top_s": s, "tree_nodes": T, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.dh, "prefix_len": [int(ax["prefix_len"].min()),
+                                                     int(ax["prefix_len"].max())],
+                   "acceptance": wl.mode, "parallelism": "single GPU"},
+        "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "heads_stage2_kernel (W2 stream + top-s)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "stages": stages,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, hx, ax, tree, cand, vlog_np, args.cpu_seconds)
+    result["setup_s"] = round(setup_s, 1)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, hx, ax, tree, cand, vlog_np, budget_s):
+    """The oracle, as it stands, on the host cores: full verify steps of the
+    same workload (same input bytes) repeated until the time budget is spent."""
+    import oracle
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], wl.s, wl.dtype)
+        oracle.tree_attention(ax["q"], ax["k_cache"], ax["v_cache"], ax["prefix_len"],
+                              ax["k_tree"], ax["v_tree"], tree.parent, wl.scale, wl.dtype)
+        oracle.tree_accept(vlog_np, cand, tree.parent, wl.dtype, wl.mode, wl.temperature)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(reps / el, 4), "unit": "steps/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full verify step(s) of {wl.name} (all heads, every attention "
+                      f"row, acceptance) in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

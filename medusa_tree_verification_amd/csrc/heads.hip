@@ -14,25 +14,43 @@
 //   splitting the d reduction; LDS sum; epilogue z = SiLU(u) + h written to
 //   the workspace (bf16 rounding once, in bf16 mode).  Also clears the
 //   per-head arrival counters used by stage 2.
-// Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over P
-//   workgroups (P waves of work per CU pair); each wave streams its tiles
-//   with several 16-byte loads in flight, keeps a per-lane top-s list of its
-//   column, merges lists across lanes (shuffles) and waves (LDS), and writes
-//   one partial list per (head, sequence) for its workgroup.  The last
-//   workgroup to finish a head (device-scope counter) merges that head's
-//   partial lists into topk_ids / topk_vals.
+// Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over one
+//   workgroup of four waves per CU (measured: more concurrent waves streaming
+//   16-row tiles lose HBM efficiency).  Each wave streams up to four tiles at
+//   a time in batches of 8 k-steps (32 KB of loads in flight, issued ahead of
+//   the MFMAs), starting at a per-wave rotated batch so that lockstep waves
+//   hit different HBM channels; it keeps a per-lane top-s list of its column,
+//   merges lists across lanes (shuffles) and waves (LDS), and writes one
+//   partial list per (head, sequence) for its workgroup.  The last workgroup
+//   to finish a head (device-scope counter) merges that head's partial lists
+//   into topk_ids / topk_vals.
 #include "common.h"
 
 namespace medusa {
 namespace {
 
+#ifndef MEDUSA_S2_TILES
+#define MEDUSA_S2_TILES 4
+#endif
+#ifndef MEDUSA_S2_UNROLL
+#define MEDUSA_S2_UNROLL 8
+#endif
+#ifndef MEDUSA_S2_WG_PER_CU
+#define MEDUSA_S2_WG_PER_CU 1
+#endif
+#ifndef MEDUSA_S2_WAVES
+#define MEDUSA_S2_WAVES 4
+#endif
+#ifndef MEDUSA_S2_BARRIER
+#define MEDUSA_S2_BARRIER 1
+#endif
 constexpr int kSMax = MEDUSA_MAX_TOPS;   // top-s list capacity
 constexpr int kS1Waves = 4;              // stage 1: waves per 16-row tile (split d)
 constexpr int kS1Unroll = 8;             // stage 1: k-steps in flight per wave
-constexpr int kS2Waves = 8;              // stage 2: waves per workgroup
-constexpr int kS2Tiles = 4;              // stage 2: row tiles per wave pass
-constexpr int kS2Unroll = 4;             // stage 2: k-steps in flight per wave
-constexpr int kS2MaxWG = kNumCU;         // stage 2: workgroups (one per CU)
+constexpr int kS2Waves = MEDUSA_S2_WAVES;        // stage 2: waves per workgroup
+constexpr int kS2Tiles = MEDUSA_S2_TILES;        // stage 2: row tiles per wave pass
+constexpr int kS2Unroll = MEDUSA_S2_UNROLL;      // stage 2: k-steps per batch of loads
+constexpr int kS2MaxWG = MEDUSA_S2_WG_PER_CU * kNumCU;   // stage 2: workgroups
 
 struct HeadsLayout {
     size_t z_off, cnt_off, part_off, total;
@@ -72,8 +90,10 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
     const int kspan = d / kS1Waves;
     const int kbeg = wave * kspan;
     const T *arow = w1 + ((size_t)head * d + row0 + c) * (size_t)d + kbeg + g * KC;
+    // lanes of columns >= B read column B-1: their outputs are never used, and
+    // an unconditional load keeps the loop free of exec-mask branches
     const bool bcol = c < B;
-    const T *brow = hidden + (size_t)(bcol ? c : 0) * d + kbeg + g * KC;
+    const T *brow = hidden + (size_t)(bcol ? c : B - 1) * d + kbeg + g * KC;
 
     // kspan = d/4 is a multiple of KSTEP (d % 128 == 0); the unrolled body
     // covers whole groups of kS1Unroll steps, the tail loop the rest.
@@ -84,14 +104,14 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
 #pragma unroll
         for (int u = 0; u < kS1Unroll; ++u) {
             a[u] = ld16(arow + k0 + u * KSTEP);
-            b[u] = bcol ? ld16(brow + k0 + u * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+            b[u] = ld16(brow + k0 + u * KSTEP);
         }
 #pragma unroll
         for (int u = 0; u < kS1Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
     }
     for (; k0 < kspan; k0 += KSTEP) {
         const u32x4 a = ld16(arow + k0);
-        const u32x4 b = bcol ? ld16(brow + k0) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 b = ld16(brow + k0);
         mma16_step(acc, a, b, T{});
     }
     red[wave][lane] = acc;
@@ -196,13 +216,61 @@ __device__ void group_merge(TopList &L, int s, int m0, float (&ov)[kSMax], int (
 }
 
 // ------------------------------------------------------------------ stage 2
+// acc[r] += W2 tile (tile_in_head + r) x z for r < NR: NR 16-row tiles of one
+// head streamed over the full d.  Full batches of kS2Unroll k-steps issue all
+// their loads ahead of their MFMAs; the batches start at batch `rot` and wrap
+// around, so that waves working in lockstep sit at different column offsets
+// (spreading concurrent requests over HBM channels); leftover k-steps
+// (d % batch) follow one at a time.  wbase: the head's W2 plus this lane's
+// chunk offset; brow: this lane's z column plus chunk offset.
+template <typename T, int NR>
+__device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__restrict__ wbase,
+                                             const T *__restrict__ brow, int tile_in_head, int V,
+                                             int d, int c, int rot) {
+    constexpr int KC = Elem<T>::kPer16B;
+    constexpr int KSTEP = 4 * KC;
+    constexpr int KB = KSTEP * kS2Unroll;
+    const T *arow[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        int row = (tile_in_head + r) * 16 + c;
+        row = row < V ? row : V - 1;        // rows past V: loaded, never used
+        arow[r] = wbase + (size_t)row * d;
+    }
+    const int nb = d / KB;
+    int bi = nb > 0 ? rot % nb : 0;
+    for (int i = 0; i < nb; ++i) {
+        const int k0 = bi * KB;
+        bi = bi + 1 == nb ? 0 : bi + 1;
+        u32x4 a[NR][kS2Unroll], b[kS2Unroll];
+#pragma unroll
+        for (int u = 0; u < kS2Unroll; ++u) b[u] = ld16(brow + k0 + u * KSTEP);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int u = 0; u < kS2Unroll; ++u) a[r][u] = ld16(arow[r] + k0 + u * KSTEP);
+#if MEDUSA_S2_BARRIER
+        // keep the whole batch of loads ahead of the MFMAs: more bytes in flight
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+#pragma unroll
+        for (int u = 0; u < kS2Unroll; ++u)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) mma16_step(acc[r], a[r][u], b[u], T{});
+    }
+    for (int k0 = nb * KB; k0 < d; k0 += KSTEP) {
+        const u32x4 b = ld16(brow + k0);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) mma16_step(acc[r], ld16(arow[r] + k0), b, T{});
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, float *__restrict__ logits_out,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals, uint32_t *__restrict__ counters,
     float2 *__restrict__ part, int B, int K, int d, int V, int s, int ntph, int nt, int P) {
     constexpr int KC = Elem<T>::kPer16B;
-    constexpr int KSTEP = 4 * KC;
     // per-wave merged lists: [wave][head slot 0/1][column][s]
     __shared__ float2 stage[kS2Waves][2][16][kSMax];
     __shared__ int merge_head[2];
@@ -218,17 +286,22 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const long long wg_beg = (long long)wg * nt / P, wg_end = (long long)(wg + 1) * nt / P;
     const int head_lo = (int)(wg_beg / ntph);
     const long long span = wg_end - wg_beg;
-    long long tile = wg_beg + span * wave / kS2Waves;
-    const long long wend = wg_beg + span * (wave + 1) / kS2Waves;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+    int tile = (int)(wg_beg + span * wv / kS2Waves);
+    const int wend = (int)(wg_beg + span * (wv + 1) / kS2Waves);
+#ifndef MEDUSA_S2_ROT
+#define MEDUSA_S2_ROT 1
+#endif
+    const int rot = MEDUSA_S2_ROT ? (int)(((unsigned)wg * kS2Waves + wv) * 7u) : 0;
     __syncthreads();
 
     const bool bcol = c < B;
     TopList L;
     L.clear();
-    int cur_head = tile < wend ? (int)(tile / ntph) : -1;
+    int cur_head = tile < wend ? tile / ntph : -1;
 
     while (tile < wend) {
-        const int head = (int)(tile / ntph);
+        const int head = tile / ntph;
         if (head != cur_head) {
             // flush the finished head's lists
             float ov[kSMax];
@@ -243,40 +316,22 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
             L.clear();
             cur_head = head;
         }
-        const long long head_end = (long long)(head + 1) * ntph;
-        const long long gend = tile + kS2Tiles < wend ? tile + kS2Tiles : wend;
-        const int n = (int)((gend < head_end ? gend : head_end) - tile);
-        const int tile_in_head = (int)(tile - (long long)head * ntph);
-
-        const T *arow[kS2Tiles];
-#pragma unroll
-        for (int r = 0; r < kS2Tiles; ++r) {
-            int row = (tile_in_head + r) * 16 + c;
-            row = row < V ? row : V - 1;
-            arow[r] = w2 + ((size_t)head * V + row) * (size_t)d + g * KC;
-        }
-        const T *brow = z + ((size_t)(bcol ? c : 0) * K + head) * d + g * KC;
+        const int head_end = (head + 1) * ntph;
+        const int gend = tile + kS2Tiles < wend ? tile + kS2Tiles : wend;
+        const int n = __builtin_amdgcn_readfirstlane((gend < head_end ? gend : head_end) - tile);
+        const int tile_in_head = tile - head * ntph;
 
         f32x4 acc[kS2Tiles];
 #pragma unroll
         for (int r = 0; r < kS2Tiles; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int k0 = 0; k0 < d; k0 += KSTEP * kS2Unroll) {
-            u32x4 a[kS2Tiles][kS2Unroll], b[kS2Unroll];
-#pragma unroll
-            for (int u = 0; u < kS2Unroll; ++u)
-                b[u] = bcol ? ld16(brow + k0 + u * KSTEP) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int r = 0; r < kS2Tiles; ++r)
-                if (r < n) {
-#pragma unroll
-                    for (int u = 0; u < kS2Unroll; ++u) a[r][u] = ld16(arow[r] + k0 + u * KSTEP);
-                }
-#pragma unroll
-            for (int u = 0; u < kS2Unroll; ++u)
-#pragma unroll
-                for (int r = 0; r < kS2Tiles; ++r)
-                    if (r < n) mma16_step(acc[r], a[r][u], b[u], T{});
+        const T *brow = z + ((size_t)(bcol ? c : B - 1) * K + head) * d + g * KC;
+        const T *wbase = w2 + (size_t)head * V * d + g * KC;
+        // n is wave-uniform: one straight-line body per tile count
+        switch (n) {
+            case 1: stream_tiles<T, 1>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
+            case 2: stream_tiles<T, 2>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
+            case 3: stream_tiles<T, 3>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
+            default: stream_tiles<T, kS2Tiles>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
         }
 
         // epilogue: lane holds rows 16*tile + 4g + i of column c

@@ -25,6 +25,7 @@ namespace medusa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 8;     // 16-byte loads in flight per thread in row scans
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -131,7 +132,7 @@ __device__ __forceinline__ void scan_row_chunk(const u32x4 &c, int base, int mod
         if (cm > st.m) {
             const float d = st.m - cm;
             if (st.S != 0.f) {
-                const float f = exp2f(d);
+                const float f = fast_exp2(d);
                 st.A = (st.A + d * st.S) * f;
                 st.S *= f;
             }
@@ -140,7 +141,7 @@ __device__ __forceinline__ void scan_row_chunk(const u32x4 &c, int base, int mod
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float dd = x[e] - st.m;
-            const float ex = exp2f(dd);
+            const float ex = fast_exp2(dd);
             st.S += ex;
             st.A += ex * dd;
         }
@@ -187,12 +188,12 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
     if (vec) {
         const int nch = p.V / E;
         int ch = threadIdx.x;
-        for (; ch + 3 * kThreads < nch; ch += 4 * kThreads) {
-            u32x4 c[4];
+        for (; ch + (kUnroll - 1) * kThreads < nch; ch += kUnroll * kThreads) {
+            u32x4 c[kUnroll];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) c[u] = ld16(row + (size_t)(ch + u * kThreads) * E);
+            for (int u = 0; u < kUnroll; ++u) c[u] = ld16(row + (size_t)(ch + u * kThreads) * E);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < kUnroll; ++u)
                 scan_row_chunk<T>(c[u], (ch + u * kThreads) * E, p.mode, p.zscale, am, st);
         }
         for (; ch < nch; ch += kThreads)
@@ -293,7 +294,18 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
     ArgMax am{-INFINITY, 0x7FFFFFFF};
     constexpr int E = Elem<T>::kPer16B;
     if (p.V % E == 0) {
-        for (int ch = threadIdx.x; ch < p.V / E; ch += kThreads) {
+        const int nch = p.V / E;
+        int ch = threadIdx.x;
+        for (; ch + (kUnroll - 1) * kThreads < nch; ch += kUnroll * kThreads) {
+            u32x4 c[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) c[u] = ld16(row + (size_t)(ch + u * kThreads) * E);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c[u], e), (ch + u * kThreads) * E + e);
+        }
+        for (; ch < nch; ch += kThreads) {
             const u32x4 c = ld16(row + (size_t)ch * E);
 #pragma unroll
             for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c, e), ch * E + e);

@@ -72,46 +72,78 @@ __device__ __forceinline__ int vt_pos<bf16_t>(int k) {
     return (k & ~15) + 8 * (a & 1) + 4 * (a >> 1) + (k & 3);
 }
 
-// Stage keys [k0, k0 + nvalid) of one (b, kv head) into LDS: K as rows, V
-// transposed.  Rows past nvalid are zero (their scores are masked; zero V
-// keeps 0 * garbage out of the sums).
-template <typename T, int DH>
-__device__ __forceinline__ void stage_block(char *lds, const T *__restrict__ kb,
-                                            const T *__restrict__ vb, int nvalid, int tid,
-                                            int nthr) {
+// Register-staged copy of one 64-key stage (keys [0, nvalid) from kb / vb) to
+// LDS: K as rows, V transposed.  load() issues every global load of the
+// stage at once (so one memory latency covers the stage and the loads can
+// fly while the previous stage is computed); store() writes them to LDS.
+// Rows past nvalid are zero: their scores are masked, and zero V keeps
+// 0 * garbage out of the sums.  NT = threads of the workgroup.
+template <typename T, int DH, int NT>
+struct StageCopy {
     using C = Cfg<T, DH>;
-    char *Ks = lds;
-    char *Vt = lds + C::KS_BYTES;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int ch = tid; ch < kBN * C::CPR; ch += nthr) {
-        const int key = ch / C::CPR, col = ch % C::CPR;
-        const u32x4 v = key < nvalid ? ld16(kb + (size_t)key * DH + col * C::KC) : zero;
-        st16(Ks + key * C::KS_STRIDE + col * 16, v);
-    }
-    // V: a unit is 4 consecutive keys x one 16-byte column chunk
-    for (int u = tid; u < (kBN / 4) * C::CPR; u += nthr) {
-        const int col = u % C::CPR, kg = u / C::CPR;
-        u32x4 r[4];
+    static constexpr int NK = (kBN * C::CPR + NT - 1) / NT;          // K chunks / thread
+    static constexpr int NV = ((kBN / 4) * C::CPR + NT - 1) / NT;    // V units / thread
+    u32x4 k[NK];
+    u32x4 v[NV][4];
+
+    __device__ __forceinline__ void load(const T *__restrict__ kb, const T *__restrict__ vb,
+                                         int nvalid, int tid) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = 4 * kg + j;
-            r[j] = key < nvalid ? ld16(vb + (size_t)key * DH + col * C::KC) : zero;
+        for (int i = 0; i < NK; ++i) {
+            const int ch = tid + i * NT;
+            const int key = ch / C::CPR, col = ch % C::CPR;
+            k[i] = (ch < kBN * C::CPR && key < nvalid) ? ld16(kb + (size_t)key * DH + col * C::KC)
+                                                       : zero;
         }
-        const int pos = vt_pos<T>(4 * kg);
 #pragma unroll
-        for (int e = 0; e < C::KC; ++e) {
-            char *dst = Vt + (col * C::KC + e) * C::VT_STRIDE + pos * (int)sizeof(T);
-            if constexpr (sizeof(T) == 2) {
-                const int w = e >> 1, sh = (e & 1) * 16;
-                const uint32_t lo = ((r[0][w] >> sh) & 0xFFFFu) | (((r[1][w] >> sh) & 0xFFFFu) << 16);
-                const uint32_t hi = ((r[2][w] >> sh) & 0xFFFFu) | (((r[3][w] >> sh) & 0xFFFFu) << 16);
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{lo, hi};
-            } else {
-                st16(dst, u32x4{r[0][e], r[1][e], r[2][e], r[3][e]});
+        for (int i = 0; i < NV; ++i) {
+            const int u = tid + i * NT;
+            const int col = u % C::CPR, kg = u / C::CPR;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = 4 * kg + j;
+                v[i][j] = (u < (kBN / 4) * C::CPR && key < nvalid)
+                              ? ld16(vb + (size_t)key * DH + col * C::KC)
+                              : zero;
             }
         }
     }
-}
+
+    __device__ __forceinline__ void store(char *lds, int tid) const {
+        char *Ks = lds;
+        char *Vt = lds + C::KS_BYTES;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int ch = tid + i * NT;
+            if (ch < kBN * C::CPR) {
+                const int key = ch / C::CPR, col = ch % C::CPR;
+                st16(Ks + key * C::KS_STRIDE + col * 16, k[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int u = tid + i * NT;
+            if (u >= (kBN / 4) * C::CPR) continue;
+            const int col = u % C::CPR, kg = u / C::CPR;
+            const int pos = vt_pos<T>(4 * kg);
+#pragma unroll
+            for (int e = 0; e < C::KC; ++e) {
+                char *dst = Vt + (col * C::KC + e) * C::VT_STRIDE + pos * (int)sizeof(T);
+                if constexpr (sizeof(T) == 2) {
+                    const int w = e >> 1, sh = (e & 1) * 16;
+                    const uint32_t lo = ((v[i][0][w] >> sh) & 0xFFFFu) |
+                                        (((v[i][1][w] >> sh) & 0xFFFFu) << 16);
+                    const uint32_t hi = ((v[i][2][w] >> sh) & 0xFFFFu) |
+                                        (((v[i][3][w] >> sh) & 0xFFFFu) << 16);
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{lo, hi};
+                } else {
+                    st16(dst, u32x4{v[i][0][e], v[i][1][e], v[i][2][e], v[i][3][e]});
+                }
+            }
+        }
+    }
+};
 
 struct RowState {
     float m;      // running max of scores * c (log2 units), shared by lane pair
@@ -129,7 +161,7 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
     const char *Ks = lds;
     const char *Vt = lds + C::KS_BYTES;
     const int h = lane >> 5, col = lane & 31;
-#pragma unroll
+#pragma unroll 1
     for (int sub = 0; sub < 2; ++sub) {
         f32x16 s = {};
         const char *krow = Ks + (sub * 32 + col) * C::KS_STRIDE + h * 16;
@@ -149,22 +181,28 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
             mx = fmaxf(mx, x[r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(st.m, mx);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(st.m - mref);
+        // Lazy rescaling: the reference max only moves when the block max
+        // exceeds it by more than 8 (log2 units), so p <= 2^8 and most blocks
+        // skip the O rescale; the branch is taken by the whole wave or not at
+        // all.  The result does not depend on the reference (exact algebra).
+        const bool need = mx > st.m + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+            const float mnew = need ? mx : st.m;
+            const float alpha = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mnew);
+            st.l *= alpha;
+            st.m = mnew;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
+        }
+        const float mref = st.m == -INFINITY ? 0.f : st.m;
         float p[16];
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = exp2f(x[r] - mref);
+            p[r] = fast_exp2(x[r] - mref);
             psum += p[r];
         }
-        st.l = st.l * alpha + psum;
-        st.m = mnew;
-        if (alpha != 1.0f) {
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
-        }
+        st.l += psum;
         // O^T[dh][q] += V^T[dh][key] P^T[key][q]
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
@@ -177,8 +215,7 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
                     u32x4 b;
 #pragma unroll
                     for (int w = 0; w < 4; ++w)
-                        b[w] = (uint32_t)f32_to_bf16(p[8 * mm + 2 * w]) |
-                               ((uint32_t)f32_to_bf16(p[8 * mm + 2 * w + 1]) << 16);
+                        b[w] = pack_bf16x2(p[8 * mm + 2 * w], p[8 * mm + 2 * w + 1]);
                     mma32_step(o[dt], a, b, T{});
                 }
             } else {
@@ -195,9 +232,12 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
     }
 }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(kMaxWaves *kWave) void tree_attn_fwd_kernel(AttnParams p) {
+// NW waves are launched per workgroup; the first p.W of them own query rows,
+// all of them share the staging of K/V.
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(NW *kWave, 2) void tree_attn_fwd_kernel(AttnParams p) {
     using C = Cfg<T, DH>;
+    constexpr int NT = NW * kWave;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
     __shared__ uint8_t par[MEDUSA_MAX_TREE];
 
@@ -241,7 +281,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void tree_attn_fwd_kernel(AttnPar
     // this lane's query row
     const int col = lane & 31, h = lane >> 5;
     const int row = mt * 32 * p.W + wave * 32 + col;
-    const bool rvalid = row < p.M;
+    const bool rvalid = wave < p.W && row < p.M;
     const int g = rvalid ? row / p.T : 0;
     const int t = rvalid ? row % p.T : 0;
     const int hq = kvh * p.G + g;
@@ -269,31 +309,49 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void tree_attn_fwd_kernel(AttnPar
     for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{};
     RowState st{-INFINITY, 0.f};
 
-    const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
-    for (int k0 = kbeg; k0 < kend; k0 += kBN) {
-        const int nv = kend - k0 < kBN ? kend - k0 : kBN;
-        __syncthreads();
-        stage_block<T, DH>(lds, (const T *)p.kc + kvbase + (size_t)k0 * DH,
-                           (const T *)p.vc + kvbase + (size_t)k0 * DH, nv, tid, nthr);
-        __syncthreads();
-        attend_stage<T, DH>(lds, qf, o, st, lane, 0, nv, 0ull, p.c);
-    }
-    if (last) {
-        const size_t tbase = ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
-        for (int tb = 0; tb < p.T; tb += kBN) {
+    // stages: prefix keys [kbeg, kend) in blocks of kBN, then (last split) the tree keys
+    const T *kcb = (const T *)p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
+    const T *vcb = (const T *)p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
+    const T *ktb = (const T *)p.kt + ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
+    const T *vtb = (const T *)p.vt + ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
+    const int npre = (kend - kbeg + kBN - 1) / kBN;
+    const int nstage = npre + (last ? (p.T + kBN - 1) / kBN : 0);
+    const bool computes = wave < p.W;
+
+    StageCopy<T, DH, NT> cp;
+    auto issue = [&](int sidx) {
+        if (sidx < npre) {
+            const int k0 = kbeg + sidx * kBN;
+            const int nv = kend - k0 < kBN ? kend - k0 : kBN;
+            cp.load(kcb + (size_t)k0 * DH, vcb + (size_t)k0 * DH, nv, tid);
+        } else {
+            const int tb = (sidx - npre) * kBN;
             const int nv = p.T - tb < kBN ? p.T - tb : kBN;
-            __syncthreads();
-            stage_block<T, DH>(lds, (const T *)p.kt + tbase + (size_t)tb * DH,
-                               (const T *)p.vt + tbase + (size_t)tb * DH, nv, tid, nthr);
-            __syncthreads();
-            const int wi = tb >> 6;
-            const uint64_t mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
-            attend_stage<T, DH>(lds, qf, o, st, lane, 1, 0, mword, p.c);
+            cp.load(ktb + (size_t)tb * DH, vtb + (size_t)tb * DH, nv, tid);
         }
+    };
+    issue(0);
+    for (int sidx = 0; sidx < nstage; ++sidx) {
+        __syncthreads();                       // everyone is done with the previous stage
+        cp.store(lds, tid);
+        __syncthreads();
+        if (sidx + 1 < nstage) issue(sidx + 1);  // in flight while this stage is computed
+        if (!computes) continue;
+        int kind = 0, klim = 0;
+        uint64_t mword = 0ull;
+        if (sidx < npre) {
+            const int k0 = kbeg + sidx * kBN;
+            klim = kend - k0 < kBN ? kend - k0 : kBN;
+        } else {
+            const int wi = sidx - npre;
+            kind = 1;
+            mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+        }
+        attend_stage<T, DH>(lds, qf, o, st, lane, kind, klim, mword, p.c);
     }
 
     const float ltot = st.l + __shfl_xor(st.l, 32);
-    if (!rvalid) return;
+    if (!rvalid || !computes) return;
     const size_t orow = ((size_t)b * p.Hq + hq) * p.T + t;
     if (nsb == 1) {
         const float inv = 1.0f / ltot;
@@ -304,10 +362,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void tree_attn_fwd_kernel(AttnPar
             for (int i = 0; i < 4; ++i) {
                 T *d4 = dst + dt * 32 + 8 * i + 4 * h;
                 if constexpr (sizeof(T) == 2) {
-                    const uint32_t lo = (uint32_t)f32_to_bf16(o[dt][4 * i] * inv) |
-                                        ((uint32_t)f32_to_bf16(o[dt][4 * i + 1] * inv) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(o[dt][4 * i + 2] * inv) |
-                                        ((uint32_t)f32_to_bf16(o[dt][4 * i + 3] * inv) << 16);
+                    const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+                    const uint32_t hi = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
                     *reinterpret_cast<u32x2 *>(d4) = u32x2{lo, hi};
                 } else {
                     *reinterpret_cast<f32x4 *>(d4) =
@@ -347,7 +403,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     float den = 0.f;
     for (int sp = 0; sp < nsb; ++sp) {
         const float2 ml = p.part_ml[(size_t)sp * nrows + rowid];
-        const float w = exp2f(ml.x - mmax);
+        const float w = fast_exp2(ml.x - mmax);
         den += w * ml.y;
         const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH;
 #pragma unroll
@@ -420,7 +476,12 @@ int check_attn(const void *q, const void *kc, const void *vc, const int32_t *pl,
 
 template <typename T, int DH>
 int launch_attn(const AttnParams &p, hipStream_t st) {
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH>), dim3(p.nwg), dim3(p.W * kWave), 0, st, p);
+    // at least four waves per workgroup so that staging a K/V block takes
+    // few loads per thread; waves beyond p.W only help staging
+    if (p.W <= 4)
+        hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, 4>), dim3(p.nwg), dim3(4 * kWave), 0, st, p);
+    else
+        hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, 8>), dim3(p.nwg), dim3(8 * kWave), 0, st, p);
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (p.nsplit > 1) {
         const size_t rows = (size_t)p.B * p.Hq * p.T;
