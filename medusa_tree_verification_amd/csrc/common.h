@@ -67,6 +67,17 @@ __device__ __forceinline__ float chunk_elem<bf16_t>(const u32x4 &c, int e) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Buffer resource over [base, base + nbytes): raw buffer loads at byte
+// offsets >= nbytes return zero (hardware range check), so tails need no
+// selects and addresses stay 32-bit offsets from an SGPR base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+                                             0x00020000 /* 32-bit data format, raw access */);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // ---------------------------------------------------------------------------

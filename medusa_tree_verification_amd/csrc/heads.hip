@@ -97,19 +97,26 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
 
     // kspan = d/4 is a multiple of KSTEP (d % 128 == 0); the unrolled body
     // covers whole groups of kS1Unroll steps, the tail loop the rest.
+    // Batches start at a per-wave rotated offset (spreads lockstep waves over
+    // HBM channels); loads of a batch are issued ahead of its MFMAs.
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int k0 = 0;
-    for (; k0 + KSTEP * kS1Unroll <= kspan; k0 += KSTEP * kS1Unroll) {
+    constexpr int KB = KSTEP * kS1Unroll;
+    const int nb = kspan / KB;
+    int bi = nb > 0 ? (int)((blockIdx.x * kS1Waves + wave) % (unsigned)nb) : 0;
+    for (int i = 0; i < nb; ++i) {
+        const int kb = bi * KB;
+        bi = bi + 1 == nb ? 0 : bi + 1;
         u32x4 a[kS1Unroll], b[kS1Unroll];
 #pragma unroll
         for (int u = 0; u < kS1Unroll; ++u) {
-            a[u] = ld16(arow + k0 + u * KSTEP);
-            b[u] = ld16(brow + k0 + u * KSTEP);
+            a[u] = ld16(arow + kb + u * KSTEP);
+            b[u] = ld16(brow + kb + u * KSTEP);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kS1Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
     }
-    for (; k0 < kspan; k0 += KSTEP) {
+    for (int k0 = nb * KB; k0 < kspan; k0 += KSTEP) {
         const u32x4 a = ld16(arow + k0);
         const u32x4 b = ld16(brow + k0);
         mma16_step(acc, a, b, T{});

@@ -25,7 +25,7 @@ namespace medusa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;     // 16-byte loads in flight per thread in row scans
+constexpr int kUnroll = 16;    // 16-byte loads in flight per thread in row scans
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -150,13 +150,16 @@ __device__ __forceinline__ void scan_row_chunk(const u32x4 &c, int base, int mod
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
-    __shared__ uint8_t par[MEDUSA_MAX_TREE], dep[MEDUSA_MAX_TREE], rk[MEDUSA_MAX_TREE];
-    __shared__ int node_sh;
+    __shared__ uint8_t par[MEDUSA_MAX_TREE];
+    __shared__ int node_sh, node_depth;
     __shared__ uint8_t is_int[kThreads];
     __shared__ int wcount[kThreads / kWave];
+    __shared__ int ccount[kThreads / kWave];
+    __shared__ int child_tok[MEDUSA_MAX_TREE];   // token of child node c (by index)
     __shared__ ArgMax red[kThreads / kWave];
     __shared__ float redS[3][kThreads / kWave];
-    load_tree(p, par, dep, rk);
+    static_assert(kThreads >= MEDUSA_MAX_TREE, "one thread per tree node");
+    for (int i = threadIdx.x; i < p.T; i += kThreads) par[i] = p.parent[i];
     const int b = blockIdx.y;
 
     // this workgroup's node: the blockIdx.x-th node (in index order) that has
@@ -179,6 +182,28 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
     __syncthreads();
     const int n = node_sh;
     if (n < 0) return;
+    // the children of n, their ranks (ballot prefix count over child flags, or
+    // node_rank) and their tokens: candidate rank(c) of head depth(n)
+    if (threadIdx.x == 0) {
+        int dn = 0;
+        for (int a = n; par[a] != 255 && dn <= p.T; a = par[a]) ++dn;
+        node_depth = dn;
+    }
+    {
+        const int c = threadIdx.x;
+        const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+        const bool child = c < p.T && c > n && par[c] == n;
+        const uint64_t bal = __ballot(child);
+        if (lane == 0) ccount[wave] = __popcll(bal);
+        __syncthreads();
+        if (child) {
+            int rank = __popcll(bal & ((1ull << lane) - 1ull));
+            for (int w = 0; w < wave; ++w) rank += ccount[w];
+            if (p.has_rank) rank = p.rank[c];
+            child_tok[c] = p.topk[((size_t)b * p.K + node_depth) * p.s + rank];
+        }
+        __syncthreads();
+    }
 
     const T *row = (const T *)p.logits + ((size_t)b * p.T + n) * p.V;
     ArgMax am{-INFINITY, 0x7FFFFFFF};
@@ -186,18 +211,21 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
     constexpr int E = Elem<T>::kPer16B;
     const bool vec = (p.V % E) == 0;
     if (vec) {
+        // whole batches of kUnroll loads per thread, the last one predicated
         const int nch = p.V / E;
-        int ch = threadIdx.x;
-        for (; ch + (kUnroll - 1) * kThreads < nch; ch += kUnroll * kThreads) {
+        for (int base = threadIdx.x; base < nch; base += kUnroll * kThreads) {
             u32x4 c[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) c[u] = ld16(row + (size_t)(ch + u * kThreads) * E);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int ch = base + u * kThreads;
+                c[u] = ch < nch ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                scan_row_chunk<T>(c[u], (ch + u * kThreads) * E, p.mode, p.zscale, am, st);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int ch = base + u * kThreads;
+                if (ch < nch) scan_row_chunk<T>(c[u], ch * E, p.mode, p.zscale, am, st);
+            }
         }
-        for (; ch < nch; ch += kThreads)
-            scan_row_chunk<T>(ld16(row + (size_t)ch * E), ch * E, p.mode, p.zscale, am, st);
     } else {
         for (int v = threadIdx.x; v < p.V; v += kThreads) {
             const float x = Elem<T>::to_f32(row[v]);
@@ -212,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
     if (p.mode == MEDUSA_GREEDY) {
         const ArgMax r = block_argmax(am, red);
         for (int c = n + 1 + (int)threadIdx.x; c < p.T; c += kThreads)
-            if (par[c] == n) p.valid[(size_t)b * p.T + c] = node_token(p, b, c, dep, rk) == r.i;
+            if (par[c] == n) p.valid[(size_t)b * p.T + c] = child_tok[c] == r.i;
     } else {
         for (int m = 32; m >= 1; m >>= 1) {
             const float m2 = __shfl_xor(st.m, m), S2 = __shfl_xor(st.S, m), A2 = __shfl_xor(st.A, m);
@@ -232,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
         const float thr = fminf(p.eps, p.delta * expf(-H));
         for (int c = n + 1 + (int)threadIdx.x; c < p.T; c += kThreads) {
             if (par[c] != n) continue;
-            const int tok = node_token(p, b, c, dep, rk);
+            const int tok = child_tok[c];
             bool ok = false;
             if (tok >= 0 && tok < p.V) {
                 const float z = Elem<T>::to_f32(row[tok]) * p.zscale;
@@ -247,23 +275,26 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
     __shared__ uint8_t par[MEDUSA_MAX_TREE], dep[MEDUSA_MAX_TREE], rk[MEDUSA_MAX_TREE];
-    __shared__ uint8_t okv[MEDUSA_MAX_TREE];
+    __shared__ uint8_t valid[MEDUSA_MAX_TREE];
+    __shared__ int cand[MEDUSA_MAX_HEADS * 256];
     __shared__ int keys[kThreads / kWave];
     __shared__ ArgMax red[kThreads / kWave];
-    load_tree(p, par, dep, rk);
     const int b = blockIdx.x;
-    const uint8_t *valid = p.valid + (size_t)b * p.T;
+    // this sequence's valid bits and candidate ids, read once into LDS
+    for (int n = threadIdx.x; n < p.T; n += kThreads) valid[n] = p.valid[(size_t)b * p.T + n];
+    for (int i = threadIdx.x; i < p.K * p.s; i += kThreads) cand[i] = p.topk[(size_t)b * p.K * p.s + i];
+    load_tree(p, par, dep, rk);   // ends with a barrier
 
     int key = -1;  // (depth << 16) | (0xFFFF - node): max = deepest, lowest index
     for (int n = threadIdx.x; n < p.T; n += kThreads) {
         bool ok = true;
         for (int a = n, g = 0; a != 0 && g <= p.T; a = par[a], ++g) ok = ok && valid[a] != 0;
-        okv[n] = ok;
         if (ok) {
             const int k = ((int)dep[n] << 16) | (0xFFFF - n);
             key = k > key ? k : key;
         }
-        if (p.node_tokens) p.node_tokens[(size_t)b * p.T + n] = node_token(p, b, n, dep, rk);
+        if (p.node_tokens)
+            p.node_tokens[(size_t)b * p.T + n] = n == 0 ? -1 : cand[(dep[n] - 1) * p.s + rk[n]];
     }
     for (int m = 32; m >= 1; m >>= 1) {
         const int o = __shfl_xor(key, m);
@@ -285,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
         if (k < bdep) {
             int a = best;
             for (int g = 0; dep[a] > k + 1 && g <= p.T; ++g) a = par[a];
-            tok = node_token(p, b, a, dep, rk);
+            tok = cand[(dep[a] - 1) * p.s + rk[a]];
         }
         p.accepted[(size_t)b * p.K + k] = tok;
     }
@@ -295,20 +326,21 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
     constexpr int E = Elem<T>::kPer16B;
     if (p.V % E == 0) {
         const int nch = p.V / E;
-        int ch = threadIdx.x;
-        for (; ch + (kUnroll - 1) * kThreads < nch; ch += kUnroll * kThreads) {
+        for (int base = threadIdx.x; base < nch; base += kUnroll * kThreads) {
             u32x4 c[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) c[u] = ld16(row + (size_t)(ch + u * kThreads) * E);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int ch = base + u * kThreads;
+                c[u] = ch < nch ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
+                const int ch = base + u * kThreads;
+                if (ch < nch) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c[u], e), (ch + u * kThreads) * E + e);
-        }
-        for (; ch < nch; ch += kThreads) {
-            const u32x4 c = ld16(row + (size_t)ch * E);
-#pragma unroll
-            for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c, e), ch * E + e);
+                    for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c[u], e), ch * E + e);
+                }
+            }
         }
     } else {
         for (int v = threadIdx.x; v < p.V; v += kThreads) am.add(Elem<T>::to_f32(row[v]), v);

@@ -28,10 +28,16 @@
 namespace medusa {
 namespace {
 
+#ifndef MEDUSA_ATTN_MIN_CHUNK
+#define MEDUSA_ATTN_MIN_CHUNK 256
+#endif
+#ifndef MEDUSA_ATTN_WG_PER_CU
+#define MEDUSA_ATTN_WG_PER_CU 1
+#endif
 constexpr int kBN = 64;          // keys per LDS stage
 constexpr int kMaxWaves = 8;     // waves per workgroup
-constexpr int kMinChunk = 256;   // smallest prefix split (keys)
-constexpr int kTargetWG = 2 * kNumCU;
+constexpr int kMinChunk = MEDUSA_ATTN_MIN_CHUNK;   // smallest prefix split (keys)
+constexpr int kTargetWG = MEDUSA_ATTN_WG_PER_CU * kNumCU;
 
 template <typename T, int DH>
 struct Cfg {
@@ -81,32 +87,32 @@ __device__ __forceinline__ int vt_pos<bf16_t>(int k) {
 template <typename T, int DH, int NT>
 struct StageCopy {
     using C = Cfg<T, DH>;
-    static constexpr int NK = (kBN * C::CPR + NT - 1) / NT;          // K chunks / thread
+    static constexpr int NK = (kBN * C::CPR) / NT;                   // K chunks / thread
+    static_assert((kBN * C::CPR) % NT == 0, "K chunks divide evenly over the threads");
     static constexpr int NV = ((kBN / 4) * C::CPR + NT - 1) / NT;    // V units / thread
     u32x4 k[NK];
     u32x4 v[NV][4];
 
-    __device__ __forceinline__ void load(const T *__restrict__ kb, const T *__restrict__ vb,
-                                         int nvalid, int tid) {
-        const u32x4 zero = {0u, 0u, 0u, 0u};
+    // kr / vr cover exactly the stage's valid key rows: rows past them read
+    // as zero.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                         int tid) {
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int ch = tid + i * NT;
             const int key = ch / C::CPR, col = ch % C::CPR;
-            k[i] = (ch < kBN * C::CPR && key < nvalid) ? ld16(kb + (size_t)key * DH + col * C::KC)
-                                                       : zero;
+            k[i] = buf_ld16(kr, (uint32_t)((key * DH + col * C::KC) * (int)sizeof(T)));
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int u = tid + i * NT;
-            const int col = u % C::CPR, kg = u / C::CPR;
+            const int kg = u % (kBN / 4), col = u / (kBN / 4);   // see store()
+            const bool live = u < (kBN / 4) * C::CPR;   // spare threads: offsets past the
+                                                       // range, dropped by the hardware
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = 4 * kg + j;
-                v[i][j] = (u < (kBN / 4) * C::CPR && key < nvalid)
-                              ? ld16(vb + (size_t)key * DH + col * C::KC)
-                              : zero;
-            }
+            for (int j = 0; j < 4; ++j)
+                v[i][j] = buf_ld16(vr, live ? (uint32_t)(((4 * kg + j) * DH + col * C::KC) * (int)sizeof(T))
+                                            : 0xFFFFFF00u);
         }
     }
 
@@ -121,11 +127,14 @@ struct StageCopy {
                 st16(Ks + key * C::KS_STRIDE + col * 16, k[i]);
             }
         }
+        // V units: the 16 consecutive threads of a key-group index kg share a
+        // column chunk, so each transposed store of 16 lanes fills 16 distinct
+        // 4-key slots of one dh row (128 contiguous bytes, no bank conflicts).
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int u = tid + i * NT;
             if (u >= (kBN / 4) * C::CPR) continue;
-            const int col = u % C::CPR, kg = u / C::CPR;
+            const int kg = u % (kBN / 4), col = u / (kBN / 4);
             const int pos = vt_pos<T>(4 * kg);
 #pragma unroll
             for (int e = 0; e < C::KC; ++e) {
@@ -150,13 +159,46 @@ struct RowState {
     float l;      // this lane's part of the softmax denominator
 };
 
-// One 64-key stage for one wave: two 32-key sub-blocks.
-// kind 0: prefix keys, valid while key < klim; kind 1: tree keys, valid where
-// the row's ancestor bit is set (mword = mask word of keys [tb, tb+64)).
+// P^T (16 probabilities of one 32-key block, this lane's query) times V^T of
+// those keys, accumulated into O^T.
+template <typename T, int DH>
+__device__ __forceinline__ void pv_block(const char *Vt, const float (&p)[16],
+                                         f32x16 (&o)[Cfg<T, DH>::NDT], int sub, int h, int col) {
+    using C = Cfg<T, DH>;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+        const char *vrow = Vt + (dt * 32 + col) * C::VT_STRIDE;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 16 * mm + 8 * h) * 2);
+                u32x4 b;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) b[w] = pack_bf16x2(p[8 * mm + 2 * w], p[8 * mm + 2 * w + 1]);
+                mma32_step(o[dt], a, b, T{});
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 8 * i + 4 * h) * 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mma32_f32_single(o[dt], __uint_as_float(a[j]), p[4 * i + j]);
+            }
+        }
+    }
+}
+
+// One 64-key stage for one wave (lane: query column col, keys of half h), as
+// two 32-key blocks: S^T = K Q^T on the matrix cores, running-max update,
+// P^T V^T.  masked: apply kind 0 (key < klim) or kind 1 (tree ancestor bits
+// of mword); full prefix stages skip masking.
 template <typename T, int DH>
 __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[Cfg<T, DH>::NKS],
                                              f32x16 (&o)[Cfg<T, DH>::NDT], RowState &st, int lane,
-                                             int kind, int klim, uint64_t mword, float c) {
+                                             bool masked, int kind, int klim, uint64_t mword,
+                                             float c) {
     using C = Cfg<T, DH>;
     const char *Ks = lds;
     const char *Vt = lds + C::KS_BYTES;
@@ -170,17 +212,19 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
             const u32x4 a = *reinterpret_cast<const u32x4 *>(krow + ks * 32);
             mma32_step(s, a, qf[ks], T{});
         }
-        // s[4i+j] = score of key sub*32 + 8i + 4h + j for this lane's query
-        float x[16];
+        // s[r]: key sub*32 + 8*(r/4) + 4h + r%4 of this stage
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool ok = kind == 0 ? key < klim : ((mword >> key) & 1ull) != 0ull;
+                s[r] = ok ? s[r] : -INFINITY;
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool ok = kind == 0 ? key < klim : ((mword >> key) & 1ull) != 0ull;
-            x[r] = ok ? s[r] * c : -INFINITY;
-            mx = fmaxf(mx, x[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;   // c > 0; log2 units
         // Lazy rescaling: the reference max only moves when the block max
         // exceeds it by more than 8 (log2 units), so p <= 2^8 and most blocks
         // skip the O rescale; the branch is taken by the whole wave or not at
@@ -194,41 +238,16 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
         }
-        const float mref = st.m == -INFINITY ? 0.f : st.m;
+        const float nref = st.m == -INFINITY ? 0.f : -st.m;
         float p[16];
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = fast_exp2(x[r] - mref);
+            p[r] = fast_exp2(fmaf(s[r], c, nref));
             psum += p[r];
         }
         st.l += psum;
-        // O^T[dh][q] += V^T[dh][key] P^T[key][q]
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-            const char *vrow = Vt + (dt * 32 + col) * C::VT_STRIDE;
-            if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        vrow + (sub * 32 + 16 * mm + 8 * h) * 2);
-                    u32x4 b;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        b[w] = pack_bf16x2(p[8 * mm + 2 * w], p[8 * mm + 2 * w + 1]);
-                    mma32_step(o[dt], a, b, T{});
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        vrow + (sub * 32 + 8 * i + 4 * h) * 4);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        mma32_f32_single(o[dt], __uint_as_float(a[j]), p[4 * i + j]);
-                }
-            }
-        }
+        pv_block<T, DH>(Vt, p, o, sub, h, col);
     }
 }
 
@@ -238,7 +257,7 @@ template <typename T, int DH, int NW>
 __global__ __launch_bounds__(NW *kWave, 2) void tree_attn_fwd_kernel(AttnParams p) {
     using C = Cfg<T, DH>;
     constexpr int NT = NW * kWave;
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
     __shared__ uint8_t par[MEDUSA_MAX_TREE];
 
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -320,34 +339,49 @@ __global__ __launch_bounds__(NW *kWave, 2) void tree_attn_fwd_kernel(AttnParams 
 
     StageCopy<T, DH, NT> cp;
     auto issue = [&](int sidx) {
+        const T *kb, *vb;
+        int nv;
         if (sidx < npre) {
             const int k0 = kbeg + sidx * kBN;
-            const int nv = kend - k0 < kBN ? kend - k0 : kBN;
-            cp.load(kcb + (size_t)k0 * DH, vcb + (size_t)k0 * DH, nv, tid);
+            nv = kend - k0 < kBN ? kend - k0 : kBN;
+            kb = kcb + (size_t)k0 * DH;
+            vb = vcb + (size_t)k0 * DH;
         } else {
             const int tb = (sidx - npre) * kBN;
-            const int nv = p.T - tb < kBN ? p.T - tb : kBN;
-            cp.load(ktb + (size_t)tb * DH, vtb + (size_t)tb * DH, nv, tid);
+            nv = p.T - tb < kBN ? p.T - tb : kBN;
+            kb = ktb + (size_t)tb * DH;
+            vb = vtb + (size_t)tb * DH;
         }
+        const uint32_t nbytes = (uint32_t)(nv * DH * (int)sizeof(T));
+        cp.load(make_rsrc(kb, nbytes), make_rsrc(vb, nbytes), tid);
     };
+    // Double-buffered stages, one barrier each: stage i is computed from
+    // buffer i%2 while stage i+1 (loaded during stage i-1) is written to the
+    // other buffer and stage i+2's loads are in flight.
     issue(0);
+    cp.store(lds[0], tid);
+    if (nstage > 1) issue(1);
+    __syncthreads();
     for (int sidx = 0; sidx < nstage; ++sidx) {
-        __syncthreads();                       // everyone is done with the previous stage
-        cp.store(lds, tid);
-        __syncthreads();
-        if (sidx + 1 < nstage) issue(sidx + 1);  // in flight while this stage is computed
-        if (!computes) continue;
-        int kind = 0, klim = 0;
-        uint64_t mword = 0ull;
-        if (sidx < npre) {
-            const int k0 = kbeg + sidx * kBN;
-            klim = kend - k0 < kBN ? kend - k0 : kBN;
-        } else {
-            const int wi = sidx - npre;
-            kind = 1;
-            mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+        if (computes) {
+            int kind = 0, klim = kBN;
+            uint64_t mword = 0ull;
+            if (sidx < npre) {
+                const int k0 = kbeg + sidx * kBN;
+                klim = kend - k0 < kBN ? kend - k0 : kBN;
+            } else {
+                const int wi = sidx - npre;
+                kind = 1;
+                mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+            }
+            const bool masked = kind == 1 || klim < kBN;
+            attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword, p.c);
         }
-        attend_stage<T, DH>(lds, qf, o, st, lane, kind, klim, mword, p.c);
+        if (sidx + 1 < nstage) {
+            cp.store(lds[(sidx + 1) & 1], tid);
+            if (sidx + 2 < nstage) issue(sidx + 2);
+        }
+        __syncthreads();
     }
 
     const float ltot = st.l + __shfl_xor(st.l, 32);
@@ -429,7 +463,10 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int Lcap, int dh, int T, int dtype) {
     P.nmt = (P.M + 32 * P.W - 1) / (32 * P.W);
     const long long base = (long long)B * Hkv * P.nmt;
     int want = (int)((kTargetWG + base - 1) / base);
-    const int cap = Lcap > 0 ? (Lcap + kMinChunk - 1) / kMinChunk : 1;
+    // each split writes M rows of fp32 partials: with many rows per kv head
+    // keep splits long so that the partials stay small next to the K/V bytes
+    const int min_chunk = P.M > 128 ? 2 * kMinChunk : kMinChunk;
+    const int cap = Lcap > 0 ? (Lcap + min_chunk - 1) / min_chunk : 1;
     want = want < 1 ? 1 : (want > cap ? cap : want);
     if (Lcap <= 0) {
         P.chunk = kBN;
