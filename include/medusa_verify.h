@@ -87,8 +87,8 @@ typedef enum {
  * fp32 and not rounded.  Limits: 1 <= B <= 16, 1 <= K <= 16,
  * 128 <= d <= 16384 with d % 128 == 0, s <= V, 1 <= s <= 8.
  * Kernels: stage 1 (W1 stream + SiLU + residual -> z in the workspace),
- * stage 2 (W2 stream on the matrix cores, fused top-s, last-arriving
- * workgroup of each head merges the per-workgroup lists).
+ * stage 2 (W2 stream on the matrix cores with a fused per-workgroup top-s)
+ * and a small merge of each head's per-workgroup lists.
  * ---------------------------------------------------------------------- */
 int medusa_heads_topk(const void *hidden, const void *w1, const void *w2, int B, int K, int d,
                       int V, int s, int dtype, float *logits_out, int32_t *topk_ids,

@@ -12,8 +12,7 @@
 //
 // Stage 1: grid of 16-row tiles over the K*d rows of W1, four waves per tile
 //   splitting the d reduction; LDS sum; epilogue z = SiLU(u) + h written to
-//   the workspace (bf16 rounding once, in bf16 mode).  Also clears the
-//   per-head arrival counters used by stage 2.
+//   the workspace (bf16 rounding once, in bf16 mode).
 // Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over one
 //   workgroup of four waves per CU (measured: more concurrent waves streaming
 //   16-row tiles lose HBM efficiency).  Each wave streams up to four tiles at
@@ -21,9 +20,10 @@
 //   the MFMAs), starting at a per-wave rotated batch so that lockstep waves
 //   hit different HBM channels; it keeps a per-lane top-s list of its column,
 //   merges lists across lanes (shuffles) and waves (LDS), and writes one
-//   partial list per (head, sequence) for its workgroup.  The last workgroup
-//   to finish a head (device-scope counter) merges that head's partial lists
-//   into topk_ids / topk_vals.
+//   partial list per (head, sequence) for its workgroup.  A small merge
+//   kernel (one workgroup per head) then reduces each head's partial lists
+//   into topk_ids / topk_vals: cheaper than having the last workgroup of a
+//   head merge them, whose device-scope fences cost more than a launch.
 #include "common.h"
 
 namespace medusa {
@@ -53,7 +53,7 @@ constexpr int kS2Unroll = MEDUSA_S2_UNROLL;      // stage 2: k-steps per batch o
 constexpr int kS2MaxWG = MEDUSA_S2_WG_PER_CU * kNumCU;   // stage 2: workgroups
 
 struct HeadsLayout {
-    size_t z_off, cnt_off, part_off, total;
+    size_t z_off, part_off, total;
     int ntph, nt, P;
 };
 
@@ -65,8 +65,7 @@ inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype) {
     L.nt = K * L.ntph;
     L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
     L.z_off = 0;
-    L.cnt_off = align_up((size_t)B * K * d * esize(dtype), 256);
-    L.part_off = L.cnt_off + align_up((size_t)K * sizeof(uint32_t), 256);
+    L.part_off = align_up((size_t)B * K * d * esize(dtype), 256);
     L.total = L.part_off + align_up((size_t)K * B * L.P * kSMax * 2 * sizeof(float), 256);
     return L;
 }
@@ -74,8 +73,8 @@ inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype) {
 // ------------------------------------------------------------------ stage 1
 template <typename T>
 __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
-    const T *__restrict__ hidden, const T *__restrict__ w1, T *__restrict__ z,
-    uint32_t *__restrict__ counters, int B, int K, int d) {
+    const T *__restrict__ hidden, const T *__restrict__ w1, T *__restrict__ z, int B, int K,
+    int d) {
     constexpr int KC = Elem<T>::kPer16B;  // elements per lane per k-step
     constexpr int KSTEP = 4 * KC;         // k per step (4 lane groups)
     __shared__ f32x4 red[kS1Waves][kWave];
@@ -85,7 +84,6 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
     const int tile = blockIdx.x;                 // 16 rows of the K*d row space
     const int head = (tile * 16) / d;
     const int row0 = tile * 16 - head * d;      // first row within the head
-    if (blockIdx.x == 0 && threadIdx.x < K) counters[threadIdx.x] = 0u;
 
     const int kspan = d / kS1Waves;
     const int kbeg = wave * kspan;
@@ -272,15 +270,51 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
     }
 }
 
+// Merge the partial top-s lists of head `head` (one per workgroup owning a
+// tile of it) into topk_ids / topk_vals: wave `wave` takes columns wave,
+// wave + kS2Waves, ...
+__device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part,
+                                                 int32_t *__restrict__ topk_ids,
+                                                 float *__restrict__ topk_vals, int head, int B,
+                                                 int K, int s, int ntph, int nt, int P, int wave,
+                                                 int lane) {
+    const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
+    const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
+    const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
+    const int nparts = wg_last - wg_first + 1;
+    for (int col = wave; col < B; col += kS2Waves) {
+        TopList M;
+        M.clear();
+        const float2 *src = part + ((size_t)head * B + col) * P * kSMax;
+        for (int p = lane; p < nparts; p += kWave)
+#pragma unroll
+            for (int r = 0; r < kSMax; ++r) {
+                if (r >= s) continue;
+                const float2 e = src[(size_t)p * kSMax + r];
+                const int id = __float_as_int(e.y);
+                if (id != 0x7FFFFFFF) M.insert(e.x, id, s);
+            }
+        float ov[kSMax];
+        int oi[kSMax];
+        group_merge(M, s, 1, ov, oi);
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < kSMax; ++r) {
+                if (r >= s) continue;
+                topk_ids[((size_t)col * K + head) * s + r] = oi[r];
+                if (topk_vals) topk_vals[((size_t)col * K + head) * s + r] = ov[r];
+            }
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, float *__restrict__ logits_out,
-    int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals, uint32_t *__restrict__ counters,
     float2 *__restrict__ part, int B, int K, int d, int V, int s, int ntph, int nt, int P) {
     constexpr int KC = Elem<T>::kPer16B;
     // per-wave merged lists: [wave][head slot 0/1][column][s]
     __shared__ float2 stage[kS2Waves][2][16][kSMax];
-    __shared__ int merge_head[2];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int g = lane / 16, c = lane % 16;
@@ -288,7 +322,6 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
 
     for (int i = threadIdx.x; i < kS2Waves * 2 * 16 * kSMax; i += blockDim.x)
         (&stage[0][0][0][0])[i] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
-    if (threadIdx.x < 2) merge_head[threadIdx.x] = -1;
 
     const long long wg_beg = (long long)wg * nt / P, wg_end = (long long)(wg + 1) * nt / P;
     const int head_lo = (int)(wg_beg / ntph);
@@ -408,53 +441,15 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
             }
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x < nslot) {
-        const int head = head_lo + threadIdx.x;
-        const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
-        const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
-        const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
-        const uint32_t need = (uint32_t)(wg_last - wg_first + 1);
-        const uint32_t old = atomicAdd(&counters[head], 1u);
-        merge_head[threadIdx.x] = (old + 1 == need) ? head : -1;
-    }
-    __syncthreads();
+}
 
-    // the last workgroup of a head merges its partial lists: one wave per column
-    for (int slot = 0; slot < nslot; ++slot) {
-        const int head = merge_head[slot];
-        if (head < 0) continue;
-        __threadfence();
-        const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
-        const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
-        const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
-        const int nparts = wg_last - wg_first + 1;
-        for (int col = wave; col < B; col += kS2Waves) {
-            TopList M;
-            M.clear();
-            const float2 *src = part + ((size_t)head * B + col) * P * kSMax;
-            for (int p = lane; p < nparts; p += kWave)
-#pragma unroll
-                for (int r = 0; r < kSMax; ++r) {
-                    if (r >= s) continue;
-                    const float2 e = src[(size_t)p * kSMax + r];
-                    const int id = __float_as_int(e.y);
-                    if (id != 0x7FFFFFFF) M.insert(e.x, id, s);
-                }
-            float ov[kSMax];
-            int oi[kSMax];
-            group_merge(M, s, 1, ov, oi);
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < kSMax; ++r) {
-                    if (r >= s) continue;
-                    topk_ids[((size_t)col * K + head) * s + r] = oi[r];
-                    if (topk_vals) topk_vals[((size_t)col * K + head) * s + r] = ov[r];
-                }
-            }
-        }
-    }
+// The final top-s of one head: the per-workgroup partial lists of the
+// workgroups that own its tiles, merged with one wave per column.
+__global__ __launch_bounds__(kS2Waves *kWave) void heads_merge_kernel(
+    const float2 *__restrict__ part, int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals,
+    int B, int K, int s, int ntph, int nt, int P) {
+    merge_head_lists(part, topk_ids, topk_vals, (int)blockIdx.x, B, K, s, ntph, nt, P,
+                     (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
 }
 
 // --------------------------------------------------------------- host side
@@ -479,14 +474,13 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
                   void *ws, hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype);
     char *base = (char *)ws;
-    uint32_t *cnt = (uint32_t *)(base + L.cnt_off);
     const dim3 grid((unsigned)((size_t)K * d / 16)), block(kS1Waves * kWave);
     if (dtype == MEDUSA_BF16)
         hipLaunchKernelGGL(heads_stage1_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)hidden,
-                           (const bf16_t *)w1, (bf16_t *)(base + L.z_off), cnt, B, K, d);
+                           (const bf16_t *)w1, (bf16_t *)(base + L.z_off), B, K, d);
     else
         hipLaunchKernelGGL(heads_stage1_kernel<float>, grid, block, 0, st, (const float *)hidden,
-                           (const float *)w1, (float *)(base + L.z_off), cnt, B, K, d);
+                           (const float *)w1, (float *)(base + L.z_off), B, K, d);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
@@ -494,17 +488,19 @@ int launch_stage2(const void *w2, int B, int K, int d, int V, int s, int dtype, 
                   int32_t *topk_ids, float *topk_vals, void *ws, hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype);
     char *base = (char *)ws;
-    uint32_t *cnt = (uint32_t *)(base + L.cnt_off);
     float2 *part = (float2 *)(base + L.part_off);
     const dim3 grid((unsigned)L.P), block(kS2Waves * kWave);
     if (dtype == MEDUSA_BF16)
         hipLaunchKernelGGL(heads_stage2_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)w2,
-                           (const bf16_t *)(base + L.z_off), logits_out, topk_ids, topk_vals, cnt,
-                           part, B, K, d, V, s, L.ntph, L.nt, L.P);
+                           (const bf16_t *)(base + L.z_off), logits_out, part, B, K, d, V, s,
+                           L.ntph, L.nt, L.P);
     else
         hipLaunchKernelGGL(heads_stage2_kernel<float>, grid, block, 0, st, (const float *)w2,
-                           (const float *)(base + L.z_off), logits_out, topk_ids, topk_vals, cnt,
-                           part, B, K, d, V, s, L.ntph, L.nt, L.P);
+                           (const float *)(base + L.z_off), logits_out, part, B, K, d, V, s,
+                           L.ntph, L.nt, L.P);
+    if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
+    hipLaunchKernelGGL(heads_merge_kernel, dim3((unsigned)K), block, 0, st, part, topk_ids,
+                       topk_vals, B, K, s, L.ntph, L.nt, L.P);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

@@ -11,60 +11,50 @@
 // tutorial page, section 5.3 verification loop) and the longest such path
 // wins (aiunderstanding page: accept the longest matching prefix).
 //
-// Kernel 1 (rows): one workgroup per (internal node, sequence).  A single
-//   streaming pass over the node's V logits computes the argmax, or the
-//   running (max m, S = sum e^(z-m), A = sum e^(z-m)(z-m)) from which
-//   H = ln S - A/S, and writes the valid bit of each child.
-// Kernel 2 (scan): one workgroup per sequence: each thread takes one node,
-//   ANDs the valid bits up its path, a block reduction picks the deepest
-//   reachable node (lowest index on ties); then the accepted tokens, the
-//   node tokens and the argmax of the best node's row (next token).
+// Kernel 1 (stats): one workgroup per (vocabulary chunk, node, sequence);
+//   nodes without children exit at once.  A single streaming pass over the
+//   chunk of the node's logits row records the raw maximum and its index and
+//   the running softmax statistics in the log2 domain, m = max z,
+//   S = sum 2^(z-m), A = sum 2^(z-m) (z-m) with z = x log2(e) / temperature,
+//   so that H = (log2 S - A/S) ln 2.  Many small workgroups keep the HBM
+//   busy even when a batch has few internal nodes.
+// Kernel 2 (finish): one workgroup per sequence merges each internal node's
+//   chunk statistics (staged in LDS), decides every child (typical mode reads
+//   the one logit of the child's token), ANDs the valid bits up each node's
+//   path, picks the deepest reachable node (lowest index on ties) and writes
+//   the accepted tokens, the node tokens and the next token (the best node's
+//   argmax: from its statistics when it has children, else from its row).
 #include "common.h"
 
 namespace medusa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 16;    // 16-byte loads in flight per thread in row scans
+constexpr int kUnroll = 8;           // 16-byte loads in flight per thread
+constexpr int kChunkAlign = 2048;    // vocabulary chunk granularity (elements)
+constexpr int kTargetStatWG = 2048;  // aim for about this many stats workgroups
+constexpr int kMaxStats = 2048;      // T * nchunk bound (LDS of the finish kernel)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+struct RowStat {           // 32 bytes
+    float xmax;            // largest raw logit of the chunk
+    int arg;               // its index (smallest on ties)
+    float m, S, A;         // softmax statistics (typical mode)
+    float pad[3];
+};
 
 struct AcceptParams {
     const void *logits;
     const int32_t *topk;
-    uint8_t *valid;   // [B][T]
+    RowStat *stats;        // [B][T][nchunk]
     int32_t *accept_len, *best_node, *accepted, *node_tokens, *next_token;
-    int B, T, V, K, s, mode, has_rank;
-    float zscale;     // log2(e) / temperature
+    int B, T, V, K, s, mode, has_rank, nchunk, chunk;
+    float zscale;          // log2(e) / temperature
     float eps, delta;
-    uint8_t parent[MEDUSA_MAX_TREE];  // 255 = root
+    uint8_t parent[MEDUSA_MAX_TREE];  // 255 marks the root (never a parent: parent < n <= 255)
     uint8_t rank[MEDUSA_MAX_TREE];
 };
-
-__device__ __forceinline__ void load_tree(const AcceptParams &p, uint8_t *par, uint8_t *dep,
-                                          uint8_t *rk) {
-    for (int i = threadIdx.x; i < p.T; i += blockDim.x) par[i] = p.parent[i];
-    __syncthreads();
-    for (int n = threadIdx.x; n < p.T; n += blockDim.x) {
-        int d = 0;
-        for (int a = n; par[a] != 255 && d <= p.T; a = par[a]) ++d;
-        dep[n] = (uint8_t)d;
-        int r = 0;
-        if (p.has_rank) {
-            r = p.rank[n];
-        } else if (n > 0) {
-            for (int m = 1; m < n; ++m) r += par[m] == par[n];
-        }
-        rk[n] = (uint8_t)r;
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int node_token(const AcceptParams &p, int b, int n, const uint8_t *dep,
-                                          const uint8_t *rk) {
-    if (n == 0) return -1;
-    return p.topk[((size_t)b * p.K + dep[n] - 1) * p.s + rk[n]];
-}
 
 // (value, index) argmax with the smaller index winning ties
 struct ArgMax {
@@ -78,21 +68,7 @@ struct ArgMax {
     }
 };
 
-__device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
-    for (int m = 32; m >= 1; m >>= 1) {
-        ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
-        a.add(o.v, o.i);
-    }
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    if (lane == 0) sh[wave] = a;
-    __syncthreads();
-    ArgMax r = sh[0];
-    for (int w = 1; w < (int)(blockDim.x / kWave); ++w) r.add(sh[w].v, sh[w].i);
-    __syncthreads();
-    return r;
-}
-
-// running softmax statistics in log2 units: m, S = sum 2^(x-m), A = sum 2^(x-m)(x-m)
+// running softmax statistics in log2 units
 struct SoftStats {
     float m, S, A;
     __device__ void merge(float m2, float S2, float A2) {
@@ -112,17 +88,31 @@ struct SoftStats {
     }
 };
 
+__device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
+    for (int m = 32; m >= 1; m >>= 1) {
+        ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
+        a.add(o.v, o.i);
+    }
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0) sh[wave] = a;
+    __syncthreads();
+    ArgMax r = sh[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r.add(sh[w].v, sh[w].i);
+    __syncthreads();
+    return r;
+}
+
 template <typename T>
-__device__ __forceinline__ void scan_row_chunk(const u32x4 &c, int base, int mode, float zs,
-                                               ArgMax &am, SoftStats &st) {
+__device__ __forceinline__ void add_chunk(const u32x4 &c, int base, bool typical, float zs,
+                                          ArgMax &am, SoftStats &st) {
     constexpr int E = Elem<T>::kPer16B;
     float x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = chunk_elem<T>(c, e);
-    if (mode == MEDUSA_GREEDY) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) am.add(x[e], base + e);
-    } else {
+    for (int e = 0; e < E; ++e) {
+        x[e] = chunk_elem<T>(c, e);
+        am.add(x[e], base + e);
+    }
+    if (typical) {
         float cm = -INFINITY;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -148,100 +138,60 @@ __device__ __forceinline__ void scan_row_chunk(const u32x4 &c, int base, int mod
     }
 }
 
+// Raw argmax and (typical) softmax statistics of row[lo, hi), this thread's
+// share of the whole workgroup's pass.  16-byte loads need V % E == 0 (rows
+// then start 16-byte aligned) and E-aligned bounds; otherwise element loads.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
-    __shared__ uint8_t par[MEDUSA_MAX_TREE];
-    __shared__ int node_sh, node_depth;
-    __shared__ uint8_t is_int[kThreads];
-    __shared__ int wcount[kThreads / kWave];
-    __shared__ int ccount[kThreads / kWave];
-    __shared__ int child_tok[MEDUSA_MAX_TREE];   // token of child node c (by index)
-    __shared__ ArgMax red[kThreads / kWave];
-    __shared__ float redS[3][kThreads / kWave];
-    static_assert(kThreads >= MEDUSA_MAX_TREE, "one thread per tree node");
-    for (int i = threadIdx.x; i < p.T; i += kThreads) par[i] = p.parent[i];
-    const int b = blockIdx.y;
-
-    // this workgroup's node: the blockIdx.x-th node (in index order) that has
-    // a child.  Mark parents, then rank the marks with a ballot prefix count.
-    if (threadIdx.x == 0) node_sh = -1;
-    is_int[threadIdx.x] = 0;
-    __syncthreads();
-    if (threadIdx.x >= 1 && (int)threadIdx.x < p.T) is_int[par[threadIdx.x]] = 1;
-    __syncthreads();
-    {
-        const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-        const bool mine = is_int[threadIdx.x] != 0;
-        const uint64_t bal = __ballot(mine);
-        if (lane == 0) wcount[wave] = __popcll(bal);
-        __syncthreads();
-        int before = __popcll(bal & ((1ull << lane) - 1ull));
-        for (int w = 0; w < wave; ++w) before += wcount[w];
-        if (mine && before == (int)blockIdx.x) node_sh = threadIdx.x;
-    }
-    __syncthreads();
-    const int n = node_sh;
-    if (n < 0) return;
-    // the children of n, their ranks (ballot prefix count over child flags, or
-    // node_rank) and their tokens: candidate rank(c) of head depth(n)
-    if (threadIdx.x == 0) {
-        int dn = 0;
-        for (int a = n; par[a] != 255 && dn <= p.T; a = par[a]) ++dn;
-        node_depth = dn;
-    }
-    {
-        const int c = threadIdx.x;
-        const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-        const bool child = c < p.T && c > n && par[c] == n;
-        const uint64_t bal = __ballot(child);
-        if (lane == 0) ccount[wave] = __popcll(bal);
-        __syncthreads();
-        if (child) {
-            int rank = __popcll(bal & ((1ull << lane) - 1ull));
-            for (int w = 0; w < wave; ++w) rank += ccount[w];
-            if (p.has_rank) rank = p.rank[c];
-            child_tok[c] = p.topk[((size_t)b * p.K + node_depth) * p.s + rank];
-        }
-        __syncthreads();
-    }
-
-    const T *row = (const T *)p.logits + ((size_t)b * p.T + n) * p.V;
-    ArgMax am{-INFINITY, 0x7FFFFFFF};
-    SoftStats st{-INFINITY, 0.f, 0.f};
+__device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int hi, int V,
+                                          bool typical, float zs, ArgMax &am, SoftStats &st) {
     constexpr int E = Elem<T>::kPer16B;
-    const bool vec = (p.V % E) == 0;
-    if (vec) {
-        // whole batches of kUnroll loads per thread, the last one predicated
-        const int nch = p.V / E;
-        for (int base = threadIdx.x; base < nch; base += kUnroll * kThreads) {
+    if ((V % E) == 0 && (lo % E) == 0 && (hi % E) == 0) {
+        const int c0 = lo / E, c1 = hi / E;
+        for (int base = c0 + (int)threadIdx.x; base < c1; base += kUnroll * kThreads) {
             u32x4 c[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int ch = base + u * kThreads;
-                c[u] = ch < nch ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
+                c[u] = ch < c1 ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int ch = base + u * kThreads;
-                if (ch < nch) scan_row_chunk<T>(c[u], ch * E, p.mode, p.zscale, am, st);
+                if (ch < c1) add_chunk<T>(c[u], ch * E, typical, zs, am, st);
             }
         }
     } else {
-        for (int v = threadIdx.x; v < p.V; v += kThreads) {
+        for (int v = lo + (int)threadIdx.x; v < hi; v += kThreads) {
             const float x = Elem<T>::to_f32(row[v]);
-            if (p.mode == MEDUSA_GREEDY) {
-                am.add(x, v);
-            } else {
-                st.merge(x * p.zscale, 1.f, 0.f);
-            }
+            am.add(x, v);
+            if (typical) st.merge(x * zs, 1.f, 0.f);
         }
     }
+}
 
-    if (p.mode == MEDUSA_GREEDY) {
-        const ArgMax r = block_argmax(am, red);
-        for (int c = n + 1 + (int)threadIdx.x; c < p.T; c += kThreads)
-            if (par[c] == n) p.valid[(size_t)b * p.T + c] = child_tok[c] == r.i;
-    } else {
+template <typename T>
+__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
+    __shared__ int has_child;
+    __shared__ ArgMax red[kThreads / kWave];
+    __shared__ float redS[3][kThreads / kWave];
+    static_assert(kThreads >= MEDUSA_MAX_TREE, "one thread per tree node");
+    const int j = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+    if (threadIdx.x == 0) has_child = 0;
+    __syncthreads();
+    if ((int)threadIdx.x < p.T && (int)threadIdx.x > n && p.parent[threadIdx.x] == n) has_child = 1;
+    __syncthreads();
+    if (!has_child) return;
+
+    const int lo = j * p.chunk;
+    const int hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
+    const bool typical = p.mode == MEDUSA_TYPICAL;
+    const T *row = (const T *)p.logits + ((size_t)b * p.T + n) * p.V;
+    ArgMax am{-INFINITY, 0x7FFFFFFF};
+    SoftStats st{-INFINITY, 0.f, 0.f};
+    row_stats<T>(row, lo, hi, p.V, typical, p.zscale, am, st);
+
+    const ArgMax r = block_argmax(am, red);
+    if (typical) {
         for (int m = 32; m >= 1; m >>= 1) {
             const float m2 = __shfl_xor(st.m, m), S2 = __shfl_xor(st.S, m), A2 = __shfl_xor(st.A, m);
             st.merge(m2, S2, A2);
@@ -253,46 +203,111 @@ __global__ __launch_bounds__(kThreads) void accept_rows_kernel(AcceptParams p) {
             redS[2][wave] = st.A;
         }
         __syncthreads();
-        SoftStats tot{redS[0][0], redS[1][0], redS[2][0]};
-        for (int w = 1; w < kThreads / kWave; ++w) tot.merge(redS[0][w], redS[1][w], redS[2][w]);
-        // H in nats: ln S - (A/S) ln 2  (A in log2 units)
-        const float H = (log2f(tot.S) - tot.A / tot.S) * kLn2;
-        const float thr = fminf(p.eps, p.delta * expf(-H));
-        for (int c = n + 1 + (int)threadIdx.x; c < p.T; c += kThreads) {
-            if (par[c] != n) continue;
-            const int tok = child_tok[c];
-            bool ok = false;
-            if (tok >= 0 && tok < p.V) {
-                const float z = Elem<T>::to_f32(row[tok]) * p.zscale;
-                const float pc = exp2f(z - tot.m) / tot.S;
-                ok = pc > thr;
-            }
-            p.valid[(size_t)b * p.T + c] = ok;
+        if (threadIdx.x == 0) {
+            SoftStats tot{redS[0][0], redS[1][0], redS[2][0]};
+            for (int w = 1; w < kThreads / kWave; ++w) tot.merge(redS[0][w], redS[1][w], redS[2][w]);
+            st = tot;
         }
+    }
+    if (threadIdx.x == 0) {
+        RowStat out;
+        out.xmax = r.v;
+        out.arg = r.i;
+        out.m = st.m;
+        out.S = st.S;
+        out.A = st.A;
+        out.pad[0] = out.pad[1] = out.pad[2] = 0.f;
+        p.stats[((size_t)b * p.T + n) * p.nchunk + j] = out;
     }
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
+__global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p) {
     __shared__ uint8_t par[MEDUSA_MAX_TREE], dep[MEDUSA_MAX_TREE], rk[MEDUSA_MAX_TREE];
-    __shared__ uint8_t valid[MEDUSA_MAX_TREE];
+    __shared__ uint8_t is_int[MEDUSA_MAX_TREE], valid[MEDUSA_MAX_TREE];
     __shared__ int cand[MEDUSA_MAX_HEADS * 256];
+    __shared__ RowStat sst[kMaxStats];        // this sequence's chunk statistics
+    __shared__ int marg[MEDUSA_MAX_TREE];      // merged, per internal node
+    __shared__ float mm[MEDUSA_MAX_TREE], mS[MEDUSA_MAX_TREE], mthr[MEDUSA_MAX_TREE];
     __shared__ int keys[kThreads / kWave];
     __shared__ ArgMax red[kThreads / kWave];
     const int b = blockIdx.x;
-    // this sequence's valid bits and candidate ids, read once into LDS
-    for (int n = threadIdx.x; n < p.T; n += kThreads) valid[n] = p.valid[(size_t)b * p.T + n];
-    for (int i = threadIdx.x; i < p.K * p.s; i += kThreads) cand[i] = p.topk[(size_t)b * p.K * p.s + i];
-    load_tree(p, par, dep, rk);   // ends with a barrier
+    const int tid = threadIdx.x;
+    const bool typical = p.mode == MEDUSA_TYPICAL;
 
-    int key = -1;  // (depth << 16) | (0xFFFF - node): max = deepest, lowest index
-    for (int n = threadIdx.x; n < p.T; n += kThreads) {
+    if (tid < p.T) {
+        par[tid] = p.parent[tid];
+        is_int[tid] = 0;
+    }
+    for (int i = tid; i < p.K * p.s; i += kThreads) cand[i] = p.topk[(size_t)b * p.K * p.s + i];
+    __syncthreads();
+    if (tid >= 1 && tid < p.T) is_int[par[tid]] = 1;
+    __syncthreads();
+    // stage the statistics of the internal nodes
+    for (int i = tid; i < p.T * p.nchunk; i += kThreads) {
+        if (is_int[i / p.nchunk]) sst[i] = p.stats[(size_t)b * p.T * p.nchunk + i];
+    }
+    // depth and rank of every node
+    if (tid < p.T) {
+        const int n = tid;
+        int d = 0;
+        for (int a = n; par[a] != 255 && d <= p.T; a = par[a]) ++d;
+        dep[n] = (uint8_t)d;
+        int r = 0;
+        if (p.has_rank) {
+            r = p.rank[n];
+        } else if (n > 0) {
+            for (int m = 1; m < n; ++m) r += par[m] == par[n];
+        }
+        rk[n] = (uint8_t)r;
+    }
+    __syncthreads();
+    // merged statistics of each internal node, and its acceptance threshold
+    if (tid < p.T && is_int[tid]) {
+        ArgMax am{-INFINITY, 0x7FFFFFFF};
+        SoftStats st{-INFINITY, 0.f, 0.f};
+        for (int j = 0; j < p.nchunk; ++j) {
+            const RowStat &r = sst[tid * p.nchunk + j];
+            am.add(r.xmax, r.arg);
+            if (typical) st.merge(r.m, r.S, r.A);
+        }
+        marg[tid] = am.i;
+        if (typical) {
+            const float H = (log2f(st.S) - st.A / st.S) * kLn2;   // nats
+            mm[tid] = st.m;
+            mS[tid] = st.S;
+            mthr[tid] = fminf(p.eps, p.delta * expf(-H));
+        }
+    }
+    __syncthreads();
+    // valid bit of every node (the root counts as valid)
+    if (tid < p.T) {
+        const int c = tid;
+        bool ok = true;
+        if (c > 0) {
+            const int pn = par[c];
+            const int tok = cand[(dep[c] - 1) * p.s + rk[c]];
+            if (!typical) {
+                ok = tok == marg[pn];
+            } else if (tok >= 0 && tok < p.V) {
+                const T *row = (const T *)p.logits + ((size_t)b * p.T + pn) * p.V;
+                const float z = Elem<T>::to_f32(row[tok]) * p.zscale;
+                ok = exp2f(z - mm[pn]) / mS[pn] > mthr[pn];
+            } else {
+                ok = false;
+            }
+        }
+        valid[c] = ok;
+    }
+    __syncthreads();
+
+    // deepest node whose path is all valid: key (depth << 16) | (0xFFFF - node)
+    int key = -1;
+    if (tid < p.T) {
+        const int n = tid;
         bool ok = true;
         for (int a = n, g = 0; a != 0 && g <= p.T; a = par[a], ++g) ok = ok && valid[a] != 0;
-        if (ok) {
-            const int k = ((int)dep[n] << 16) | (0xFFFF - n);
-            key = k > key ? k : key;
-        }
+        if (ok) key = ((int)dep[n] << 16) | (0xFFFF - n);
         if (p.node_tokens)
             p.node_tokens[(size_t)b * p.T + n] = n == 0 ? -1 : cand[(dep[n] - 1) * p.s + rk[n]];
     }
@@ -300,58 +315,41 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
         const int o = __shfl_xor(key, m);
         key = o > key ? o : key;
     }
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = tid % kWave, wave = tid / kWave;
     if (lane == 0) keys[wave] = key;
     __syncthreads();
     int best_key = keys[0];
     for (int w = 1; w < kThreads / kWave; ++w) best_key = keys[w] > best_key ? keys[w] : best_key;
     const int best = 0xFFFF - (best_key & 0xFFFF);
     const int bdep = dep[best];
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         p.accept_len[b] = bdep;
         p.best_node[b] = best;
     }
-    for (int k = threadIdx.x; k < p.K; k += kThreads) {
+    if (tid < p.K) {
         int tok = -1;
-        if (k < bdep) {
+        if (tid < bdep) {
             int a = best;
-            for (int g = 0; dep[a] > k + 1 && g <= p.T; ++g) a = par[a];
+            for (int g = 0; dep[a] > tid + 1 && g <= p.T; ++g) a = par[a];
             tok = cand[(dep[a] - 1) * p.s + rk[a]];
         }
-        p.accepted[(size_t)b * p.K + k] = tok;
+        p.accepted[(size_t)b * p.K + tid] = tok;
     }
     if (!p.next_token) return;
+    if (is_int[best]) {
+        if (tid == 0) p.next_token[b] = marg[best];
+        return;
+    }
     const T *row = (const T *)p.logits + ((size_t)b * p.T + best) * p.V;
     ArgMax am{-INFINITY, 0x7FFFFFFF};
-    constexpr int E = Elem<T>::kPer16B;
-    if (p.V % E == 0) {
-        const int nch = p.V / E;
-        for (int base = threadIdx.x; base < nch; base += kUnroll * kThreads) {
-            u32x4 c[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int ch = base + u * kThreads;
-                c[u] = ch < nch ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int ch = base + u * kThreads;
-                if (ch < nch) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) am.add(chunk_elem<T>(c[u], e), ch * E + e);
-                }
-            }
-        }
-    } else {
-        for (int v = threadIdx.x; v < p.V; v += kThreads) am.add(Elem<T>::to_f32(row[v]), v);
-    }
+    SoftStats unused{-INFINITY, 0.f, 0.f};
+    row_stats<T>(row, 0, p.V, p.V, false, 0.f, am, unused);
     const ArgMax r = block_argmax(am, red);
-    if (threadIdx.x == 0) p.next_token[b] = r.i;
+    if (tid == 0) p.next_token[b] = r.i;
 }
 
 // host: validate the tree for acceptance (depth <= K, rank < s)
-int check_accept_tree(const int32_t *parent, const int32_t *node_rank, int T, int K, int s,
-                      int *n_internal) {
+int check_accept_tree(const int32_t *parent, const int32_t *node_rank, int T, int K, int s) {
     if (!parent) return MEDUSA_ERR_NULL;
     if (T < 1 || T > MEDUSA_MAX_TREE) return MEDUSA_ERR_SHAPE;
     if (parent[0] != -1) return MEDUSA_ERR_TREE;
@@ -371,10 +369,25 @@ int check_accept_tree(const int32_t *parent, const int32_t *node_rank, int T, in
             for (int m = 1; m < n; ++m)
                 if (parent[m] == parent[n] && node_rank[m] == node_rank[n]) return MEDUSA_ERR_TREE;
     }
-    int ni = 0;
-    for (int n = 0; n < T; ++n) ni += nchild[n] > 0;
-    *n_internal = ni;
     return MEDUSA_OK;
+}
+
+// Vocabulary chunks per row: enough stats workgroups to fill the GPU (about
+// half the nodes of a tree have children), chunks of whole kChunkAlign
+// elements, at most kMaxStats records per sequence.  Depends on (B, T, V)
+// only, so the workspace size does too.
+void accept_chunks(int B, int T, int V, int *nchunk, int *chunk) {
+    const long long rows = (long long)B * (T > 1 ? (T + 1) / 2 : 1);
+    int want = (int)((kTargetStatWG + rows - 1) / rows);
+    const int vmax = (V + kChunkAlign - 1) / kChunkAlign;
+    const int lmax = kMaxStats / T;
+    if (want > vmax) want = vmax;
+    if (want > lmax) want = lmax;
+    if (want < 1) want = 1;
+    int ch = (V + want - 1) / want;
+    ch = (ch + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    *chunk = ch;
+    *nchunk = (V + ch - 1) / ch;
 }
 
 }  // namespace
@@ -384,9 +397,9 @@ using namespace medusa;
 
 extern "C" size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s) {
     if (B < 1 || T < 1 || T > MEDUSA_MAX_TREE || V < 1 || K < 0 || s < 1) return 0;
-    (void)K;
-    (void)s;
-    return align_up((size_t)B * T, 256);
+    int nchunk, chunk;
+    accept_chunks(B, T, V, &nchunk, &chunk);
+    return align_up((size_t)B * T * nchunk * sizeof(RowStat), 256);
 }
 
 extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *parent,
@@ -405,8 +418,7 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
         !(temperature > 0.f && temperature < INFINITY && eps > 0.f && eps < INFINITY &&
           delta > 0.f && delta < INFINITY))
         return MEDUSA_ERR_PARAM;
-    int n_internal = 0;
-    int st = check_accept_tree(parent, node_rank, T, K, s, &n_internal);
+    const int st = check_accept_tree(parent, node_rank, T, K, s);
     if (st != MEDUSA_OK) return st;
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < tree_accept_workspace_bytes(B, T, V, K, s))
         return MEDUSA_ERR_WORKSPACE;
@@ -414,7 +426,7 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
     AcceptParams p;
     p.logits = logits;
     p.topk = topk_ids;
-    p.valid = (uint8_t *)ws;
+    p.stats = (RowStat *)ws;
     p.accept_len = accept_len;
     p.best_node = best_node;
     p.accepted = accepted_tokens;
@@ -430,24 +442,24 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
     p.zscale = mode == MEDUSA_TYPICAL ? kLog2e / temperature : 0.f;
     p.eps = eps;
     p.delta = delta;
+    accept_chunks(B, T, V, &p.nchunk, &p.chunk);
     for (int i = 0; i < MEDUSA_MAX_TREE; ++i) {
         p.parent[i] = i < T && parent[i] >= 0 ? (uint8_t)parent[i] : (uint8_t)255;
         p.rank[i] = (node_rank && i < T && i > 0) ? (uint8_t)node_rank[i] : (uint8_t)0;
     }
     hipStream_t sm = (hipStream_t)stream;
-    if (n_internal > 0) {
+    if (T > 1) {
+        const dim3 grid((unsigned)p.nchunk, (unsigned)T, (unsigned)B);
         if (dtype == MEDUSA_BF16)
-            hipLaunchKernelGGL(accept_rows_kernel<bf16_t>, dim3(n_internal, B), dim3(kThreads), 0,
-                               sm, p);
+            hipLaunchKernelGGL(accept_stats_kernel<bf16_t>, grid, dim3(kThreads), 0, sm, p);
         else
-            hipLaunchKernelGGL(accept_rows_kernel<float>, dim3(n_internal, B), dim3(kThreads), 0,
-                               sm, p);
+            hipLaunchKernelGGL(accept_stats_kernel<float>, grid, dim3(kThreads), 0, sm, p);
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     }
     if (dtype == MEDUSA_BF16)
-        hipLaunchKernelGGL(accept_scan_kernel<bf16_t>, dim3(B), dim3(kThreads), 0, sm, p);
+        hipLaunchKernelGGL(accept_finish_kernel<bf16_t>, dim3(B), dim3(kThreads), 0, sm, p);
     else
-        hipLaunchKernelGGL(accept_scan_kernel<float>, dim3(B), dim3(kThreads), 0, sm, p);
+        hipLaunchKernelGGL(accept_finish_kernel<float>, dim3(B), dim3(kThreads), 0, sm, p);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

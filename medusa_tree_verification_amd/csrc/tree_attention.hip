@@ -254,7 +254,7 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 // NW waves are launched per workgroup; the first p.W of them own query rows,
 // all of them share the staging of K/V.
 template <typename T, int DH, int NW>
-__global__ __launch_bounds__(NW *kWave, 2) void tree_attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_fwd_kernel(AttnParams p) {
     using C = Cfg<T, DH>;
     constexpr int NT = NW * kWave;
     __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer

@@ -71,7 +71,7 @@ def test_accept_workloads(name):
 
 @pytest.mark.parametrize("mode", ["greedy", "typical"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [1, 7, 64, 1001, 40000])
+@pytest.mark.parametrize("V", [1, 7, 64, 1001, 40000, 40001])
 def test_accept_random(mode, dtype, V):
     rng = np.random.default_rng(V)
     K, s, B = 4, 3, 3
