@@ -70,9 +70,16 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 
 // Buffer resource over [base, base + nbytes): raw buffer loads at byte
 // offsets >= nbytes return zero (hardware range check), so tails need no
-// selects and addresses stay 32-bit offsets from an SGPR base.
+// selects and addresses stay 32-bit offsets from an SGPR base.  base and
+// nbytes must be wave-uniform: they are read from the first active lane (the
+// compiler cannot always prove uniformity and would otherwise loop over the
+// distinct values of the wave around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint64_t ua = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)ua, (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)nbytes),
                                              0x00020000 /* 32-bit data format, raw access */);
 }
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {

@@ -16,21 +16,30 @@
 //   chunk of the node's logits row records the raw maximum and its index and
 //   the running softmax statistics in the log2 domain, m = max z,
 //   S = sum 2^(z-m), A = sum 2^(z-m) (z-m) with z = x log2(e) / temperature,
-//   so that H = (log2 S - A/S) ln 2.  Many small workgroups keep the HBM
-//   busy even when a batch has few internal nodes.
-// Kernel 2 (finish): one workgroup per sequence merges each internal node's
-//   chunk statistics (staged in LDS), decides every child (typical mode reads
-//   the one logit of the child's token), ANDs the valid bits up each node's
-//   path, picks the deepest reachable node (lowest index on ties) and writes
-//   the accepted tokens, the node tokens and the next token (the best node's
-//   argmax: from its statistics when it has children, else from its row).
+//   so that H = (log2 S - A/S) ln 2.  It also records the token of each
+//   child of the node and, in typical mode, the child token's logit (by the
+//   chunk that holds it).  Many small workgroups keep the HBM busy even when
+//   a batch has few internal nodes.
+// Kernel 2 (finish): one workgroup per sequence loads, in one round, the
+//   node tokens, the chunk statistics of the internal nodes and the child
+//   logits; merges the statistics per node; decides every child; ANDs the
+//   valid bits up each node's path; picks the deepest reachable node (lowest
+//   index on ties) and writes the accepted tokens, the node tokens and the
+//   next token (the best node's argmax: from its statistics when it has
+//   children, else from one pass over its row).
+// Depth, sibling rank and the has-children flag of every node come from the
+// host, which validates the tree anyway.
 #include "common.h"
 
 namespace medusa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 8;           // 16-byte loads in flight per thread
+constexpr int kThreads = 256;        // stats kernel
+constexpr int kFinThreads = 1024;    // finish kernel (4 per node for the merges; wide row scan)
+constexpr int kMergeLanes = kFinThreads / MEDUSA_MAX_TREE;
+constexpr size_t kLeafStatBytes = 16u << 20;   // leaf rows up to this size go through the stats pass
+constexpr int kUnroll = 8;           // 16-byte loads in flight per thread (stats)
+constexpr int kScanUnroll = 16;      // 16-byte loads in flight per thread (finish row scan)
 constexpr int kChunkAlign = 2048;    // vocabulary chunk granularity (elements)
 constexpr int kTargetStatWG = 2048;  // aim for about this many stats workgroups
 constexpr int kMaxStats = 2048;      // T * nchunk bound (LDS of the finish kernel)
@@ -48,13 +57,22 @@ struct AcceptParams {
     const void *logits;
     const int32_t *topk;
     RowStat *stats;        // [B][T][nchunk]
+    float *childz;         // [B][T] raw logit of node c's token in its parent's row (typical)
+    int32_t *ctok;         // [B][T] token of node c (written by its parent's first chunk)
     int32_t *accept_len, *best_node, *accepted, *node_tokens, *next_token;
-    int B, T, V, K, s, mode, has_rank, nchunk, chunk;
+    int B, T, V, K, s, mode, nchunk, chunk;
+    int leaves;            // 1: the stats pass also covers leaf rows (argmax only)
     float zscale;          // log2(e) / temperature
     float eps, delta;
     uint8_t parent[MEDUSA_MAX_TREE];  // 255 marks the root (never a parent: parent < n <= 255)
-    uint8_t rank[MEDUSA_MAX_TREE];
+    uint8_t rank[MEDUSA_MAX_TREE];    // sibling rank: index into the depth's top-s list
+    uint8_t depth[MEDUSA_MAX_TREE];
+    uint32_t internal[MEDUSA_MAX_TREE / 32];  // bit n: node n has children
 };
+
+__device__ __forceinline__ bool has_children(const AcceptParams &p, int n) {
+    return (p.internal[n >> 5] >> (n & 31)) & 1u;
+}
 
 // (value, index) argmax with the smaller index winning ties
 struct ArgMax {
@@ -88,6 +106,7 @@ struct SoftStats {
     }
 };
 
+template <int NT>
 __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
     for (int m = 32; m >= 1; m >>= 1) {
         ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
@@ -97,7 +116,7 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
     if (lane == 0) sh[wave] = a;
     __syncthreads();
     ArgMax r = sh[0];
-    for (int w = 1; w < kThreads / kWave; ++w) r.add(sh[w].v, sh[w].i);
+    for (int w = 1; w < NT / kWave; ++w) r.add(sh[w].v, sh[w].i);
     __syncthreads();
     return r;
 }
@@ -138,60 +157,89 @@ __device__ __forceinline__ void add_chunk(const u32x4 &c, int base, bool typical
     }
 }
 
-// Raw argmax and (typical) softmax statistics of row[lo, hi), this thread's
-// share of the whole workgroup's pass.  16-byte loads need V % E == 0 (rows
-// then start 16-byte aligned) and E-aligned bounds; otherwise element loads.
+// one element of a buffer as fp32 (offsets past the buffer read 0)
 template <typename T>
+__device__ __forceinline__ float buf_elem(__amdgpu_buffer_rsrc_t r, uint32_t i);
+template <>
+__device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, i * 4u, 0, 0));
+}
+template <>
+__device__ __forceinline__ float buf_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, i * 2u, 0, 0));
+}
+
+// Raw argmax and (typical) softmax statistics of row[lo, hi), this thread's
+// share of the whole workgroup's pass.  Loads go through a buffer resource
+// over exactly [lo, hi), so they need no predicate (past the end they read 0)
+// and all U of them are in flight together; only the accumulation is
+// predicated.  16-byte loads need V % E == 0 (rows then start 16-byte
+// aligned) and E-aligned bounds; otherwise element loads.
+template <typename T, int U = kUnroll, int NT = kThreads>
 __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int hi, int V,
                                           bool typical, float zs, ArgMax &am, SoftStats &st) {
     constexpr int E = Elem<T>::kPer16B;
+    const auto rs = make_rsrc(row + lo, (uint32_t)(hi - lo) * (uint32_t)sizeof(T));
     if ((V % E) == 0 && (lo % E) == 0 && (hi % E) == 0) {
-        const int c0 = lo / E, c1 = hi / E;
-        for (int base = c0 + (int)threadIdx.x; base < c1; base += kUnroll * kThreads) {
-            u32x4 c[kUnroll];
+        const int nch = (hi - lo) / E;
+        for (int base = (int)threadIdx.x; base < nch; base += U * NT) {
+            u32x4 c[U];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int ch = base + u * kThreads;
-                c[u] = ch < c1 ? ld16(row + (size_t)ch * E) : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int u = 0; u < U; ++u) c[u] = buf_ld16(rs, (uint32_t)(base + u * NT) * 16u);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int ch = base + u * kThreads;
-                if (ch < c1) add_chunk<T>(c[u], ch * E, typical, zs, am, st);
+            for (int u = 0; u < U; ++u) {
+                const int ch = base + u * NT;
+                if (ch < nch) add_chunk<T>(c[u], lo + ch * E, typical, zs, am, st);
             }
         }
     } else {
-        for (int v = lo + (int)threadIdx.x; v < hi; v += kThreads) {
-            const float x = Elem<T>::to_f32(row[v]);
-            am.add(x, v);
-            if (typical) st.merge(x * zs, 1.f, 0.f);
+        const int n = hi - lo;
+        for (int base = (int)threadIdx.x; base < n; base += U * NT) {
+            float x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = buf_elem<T>(rs, (uint32_t)(base + u * NT));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = base + u * NT;
+                if (v < n) {
+                    am.add(x[u], lo + v);
+                    if (typical) st.merge(x[u] * zs, 1.f, 0.f);
+                }
+            }
         }
     }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) {
-    __shared__ int has_child;
     __shared__ ArgMax red[kThreads / kWave];
     __shared__ float redS[3][kThreads / kWave];
-    static_assert(kThreads >= MEDUSA_MAX_TREE, "one thread per tree node");
+    static_assert(kThreads >= MEDUSA_MAX_TREE && kFinThreads % MEDUSA_MAX_TREE == 0, "one thread per tree node");
     const int j = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
-    if (threadIdx.x == 0) has_child = 0;
-    __syncthreads();
-    if ((int)threadIdx.x < p.T && (int)threadIdx.x > n && p.parent[threadIdx.x] == n) has_child = 1;
-    __syncthreads();
-    if (!has_child) return;
+    const bool internal = has_children(p, n);
+    if (!internal && !p.leaves) return;
 
     const int lo = j * p.chunk;
     const int hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
     const bool typical = p.mode == MEDUSA_TYPICAL;
     const T *row = (const T *)p.logits + ((size_t)b * p.T + n) * p.V;
+    // thread c looks up node c's token (loads issued unconditionally, before
+    // the row pass, so that their latency hides under it)
+    const int c = threadIdx.x < p.T ? (int)threadIdx.x : 0;
+    const int cpar = p.parent[c], cdep = p.depth[c];
+    const int tok = p.topk[((size_t)b * p.K + (cdep > 0 ? cdep - 1 : 0)) * p.s + p.rank[c]];
     ArgMax am{-INFINITY, 0x7FFFFFFF};
     SoftStats st{-INFINITY, 0.f, 0.f};
-    row_stats<T>(row, lo, hi, p.V, typical, p.zscale, am, st);
+    const bool st_needed = typical && internal;   // softmax statistics: internal rows only
+    row_stats<T>(row, lo, hi, p.V, st_needed, p.zscale, am, st);
+    if ((int)threadIdx.x < p.T && c > 0 && cpar == n) {
+        // the tokens of n's children, and (typical) each one's logit in this row
+        if (j == 0) p.ctok[(size_t)b * p.T + c] = tok;
+        if (typical && tok >= lo && tok < hi) p.childz[(size_t)b * p.T + c] = Elem<T>::to_f32(row[tok]);
+    }
 
-    const ArgMax r = block_argmax(am, red);
-    if (typical) {
+    const ArgMax r = block_argmax<kThreads>(am, red);
+    if (st_needed) {
         for (int m = 32; m >= 1; m >>= 1) {
             const float m2 = __shfl_xor(st.m, m), S2 = __shfl_xor(st.S, m), A2 = __shfl_xor(st.A, m);
             st.merge(m2, S2, A2);
@@ -222,61 +270,98 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) 
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p) {
-    __shared__ uint8_t par[MEDUSA_MAX_TREE], dep[MEDUSA_MAX_TREE], rk[MEDUSA_MAX_TREE];
-    __shared__ uint8_t is_int[MEDUSA_MAX_TREE], valid[MEDUSA_MAX_TREE];
-    __shared__ int cand[MEDUSA_MAX_HEADS * 256];
+__global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AcceptParams p) {
+    __shared__ uint8_t par[MEDUSA_MAX_TREE], dep[MEDUSA_MAX_TREE], valid[MEDUSA_MAX_TREE];
+    __shared__ uint8_t isint[MEDUSA_MAX_TREE];
+    __shared__ int ntok[MEDUSA_MAX_TREE];     // token of every node (root: -1)
+    __shared__ float cz[MEDUSA_MAX_TREE];     // its logit in the parent's row (typical)
     __shared__ RowStat sst[kMaxStats];        // this sequence's chunk statistics
-    __shared__ int marg[MEDUSA_MAX_TREE];      // merged, per internal node
+    __shared__ int marg[MEDUSA_MAX_TREE];     // merged, per internal node
     __shared__ float mm[MEDUSA_MAX_TREE], mS[MEDUSA_MAX_TREE], mthr[MEDUSA_MAX_TREE];
-    __shared__ int keys[kThreads / kWave];
-    __shared__ ArgMax red[kThreads / kWave];
+    __shared__ int keys[kFinThreads / kWave];
+    __shared__ ArgMax red[kFinThreads / kWave];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const bool typical = p.mode == MEDUSA_TYPICAL;
 
+    // global loads, issued before any wait: the per-node tables, tokens and
+    // child logits, then the chunk statistics (every record of the sequence;
+    // leaves' records are never read)
+    // (loaded into registers here, written to LDS after the record loads
+    // are out)
+    int rpar = 255, rint = 0, rdep = 0, rtok = -1;
+    float rcz = 0.f;
     if (tid < p.T) {
-        par[tid] = p.parent[tid];
-        is_int[tid] = 0;
-    }
-    for (int i = tid; i < p.K * p.s; i += kThreads) cand[i] = p.topk[(size_t)b * p.K * p.s + i];
-    __syncthreads();
-    if (tid >= 1 && tid < p.T) is_int[par[tid]] = 1;
-    __syncthreads();
-    // stage the statistics of the internal nodes
-    for (int i = tid; i < p.T * p.nchunk; i += kThreads) {
-        if (is_int[i / p.nchunk]) sst[i] = p.stats[(size_t)b * p.T * p.nchunk + i];
-    }
-    // depth and rank of every node
-    if (tid < p.T) {
-        const int n = tid;
-        int d = 0;
-        for (int a = n; par[a] != 255 && d <= p.T; a = par[a]) ++d;
-        dep[n] = (uint8_t)d;
-        int r = 0;
-        if (p.has_rank) {
-            r = p.rank[n];
-        } else if (n > 0) {
-            for (int m = 1; m < n; ++m) r += par[m] == par[n];
+        rpar = p.parent[tid];
+        rint = has_children(p, tid);
+        rdep = p.depth[tid];
+        // node tokens and child logits from the statistics pass (the root has
+        // neither; with T == 1 there was no statistics pass)
+        if (tid > 0) {
+            rtok = p.ctok[(size_t)b * p.T + tid];
+            rcz = p.childz[(size_t)b * p.T + tid];
         }
-        rk[n] = (uint8_t)r;
+    }
+    {
+        constexpr int kStageU = 2;   // record loads in flight per thread
+        const int nrec = p.T * p.nchunk;
+        const RowStat *src = p.stats + (size_t)b * nrec;
+        for (int i0 = tid; i0 < nrec; i0 += kStageU * kFinThreads) {
+            // indices past the end are clamped to the last record, whose
+            // copy is then written again with the same value: no predicate,
+            // so that every load is issued before the first wait
+            RowStat r[kStageU];
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kFinThreads;
+                r[u] = src[i < nrec ? i : nrec - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kFinThreads;
+                sst[i < nrec ? i : nrec - 1] = r[u];
+            }
+        }
+    }
+    if (tid < p.T) {
+        par[tid] = (uint8_t)rpar;
+        isint[tid] = (uint8_t)rint;
+        dep[tid] = (uint8_t)rdep;
+        ntok[tid] = rtok;
+        cz[tid] = rcz;
     }
     __syncthreads();
-    // merged statistics of each internal node, and its acceptance threshold
-    if (tid < p.T && is_int[tid]) {
+    // merged statistics of each node that has records (internal nodes; all
+    // nodes when the stats pass covered the leaves), and each internal
+    // node's acceptance threshold: kMergeLanes adjacent lanes per node, each
+    // merging every kMergeLanes-th chunk, then combined by shuffles
+    {
+        const int n = tid / kMergeLanes, q = tid % kMergeLanes;
+        const bool has = n < p.T && (isint[n] || p.leaves);
         ArgMax am{-INFINITY, 0x7FFFFFFF};
         SoftStats st{-INFINITY, 0.f, 0.f};
-        for (int j = 0; j < p.nchunk; ++j) {
-            const RowStat &r = sst[tid * p.nchunk + j];
-            am.add(r.xmax, r.arg);
-            if (typical) st.merge(r.m, r.S, r.A);
+        if (has) {
+            for (int j = q; j < p.nchunk; j += kMergeLanes) {
+                const RowStat &r = sst[n * p.nchunk + j];
+                am.add(r.xmax, r.arg);
+                if (typical && isint[n]) st.merge(r.m, r.S, r.A);
+            }
         }
-        marg[tid] = am.i;
-        if (typical) {
-            const float H = (log2f(st.S) - st.A / st.S) * kLn2;   // nats
-            mm[tid] = st.m;
-            mS[tid] = st.S;
-            mthr[tid] = fminf(p.eps, p.delta * expf(-H));
+#pragma unroll
+        for (int m = 1; m < kMergeLanes; m <<= 1) {
+            const ArgMax o{__shfl_xor(am.v, m), __shfl_xor(am.i, m)};
+            am.add(o.v, o.i);
+            const float m2 = __shfl_xor(st.m, m), S2 = __shfl_xor(st.S, m), A2 = __shfl_xor(st.A, m);
+            st.merge(m2, S2, A2);
+        }
+        if (has && q == 0) {
+            marg[n] = am.i;
+            if (typical && isint[n]) {
+                const float H = (log2f(st.S) - st.A / st.S) * kLn2;   // nats
+                mm[n] = st.m;
+                mS[n] = st.S;
+                mthr[n] = fminf(p.eps, p.delta * expf(-H));
+            }
         }
     }
     __syncthreads();
@@ -286,16 +371,13 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
         bool ok = true;
         if (c > 0) {
             const int pn = par[c];
-            const int tok = cand[(dep[c] - 1) * p.s + rk[c]];
-            if (!typical) {
+            const int tok = ntok[c];
+            if (!typical)
                 ok = tok == marg[pn];
-            } else if (tok >= 0 && tok < p.V) {
-                const T *row = (const T *)p.logits + ((size_t)b * p.T + pn) * p.V;
-                const float z = Elem<T>::to_f32(row[tok]) * p.zscale;
-                ok = exp2f(z - mm[pn]) / mS[pn] > mthr[pn];
-            } else {
+            else if (tok >= 0 && tok < p.V)
+                ok = exp2f(cz[c] * p.zscale - mm[pn]) / mS[pn] > mthr[pn];
+            else
                 ok = false;
-            }
         }
         valid[c] = ok;
     }
@@ -308,8 +390,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
         bool ok = true;
         for (int a = n, g = 0; a != 0 && g <= p.T; a = par[a], ++g) ok = ok && valid[a] != 0;
         if (ok) key = ((int)dep[n] << 16) | (0xFFFF - n);
-        if (p.node_tokens)
-            p.node_tokens[(size_t)b * p.T + n] = n == 0 ? -1 : cand[(dep[n] - 1) * p.s + rk[n]];
+        if (p.node_tokens) p.node_tokens[(size_t)b * p.T + n] = ntok[n];
     }
     for (int m = 32; m >= 1; m >>= 1) {
         const int o = __shfl_xor(key, m);
@@ -319,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
     if (lane == 0) keys[wave] = key;
     __syncthreads();
     int best_key = keys[0];
-    for (int w = 1; w < kThreads / kWave; ++w) best_key = keys[w] > best_key ? keys[w] : best_key;
+    for (int w = 1; w < kFinThreads / kWave; ++w) best_key = keys[w] > best_key ? keys[w] : best_key;
     const int best = 0xFFFF - (best_key & 0xFFFF);
     const int bdep = dep[best];
     if (tid == 0) {
@@ -331,30 +412,37 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptParams p)
         if (tid < bdep) {
             int a = best;
             for (int g = 0; dep[a] > tid + 1 && g <= p.T; ++g) a = par[a];
-            tok = cand[(dep[a] - 1) * p.s + rk[a]];
+            tok = ntok[a];
         }
         p.accepted[(size_t)b * p.K + tid] = tok;
     }
     if (!p.next_token) return;
-    if (is_int[best]) {
+    if (isint[best] || p.leaves) {
         if (tid == 0) p.next_token[b] = marg[best];
         return;
     }
     const T *row = (const T *)p.logits + ((size_t)b * p.T + best) * p.V;
     ArgMax am{-INFINITY, 0x7FFFFFFF};
     SoftStats unused{-INFINITY, 0.f, 0.f};
-    row_stats<T>(row, 0, p.V, p.V, false, 0.f, am, unused);
-    const ArgMax r = block_argmax(am, red);
+    row_stats<T, kScanUnroll, kFinThreads>(row, 0, p.V, p.V, false, 0.f, am, unused);
+    const ArgMax r = block_argmax<kFinThreads>(am, red);
     if (tid == 0) p.next_token[b] = r.i;
 }
 
-// host: validate the tree for acceptance (depth <= K, rank < s)
-int check_accept_tree(const int32_t *parent, const int32_t *node_rank, int T, int K, int s) {
+// host: validate the tree for acceptance (depth <= K, rank < s) and fill in
+// every node's depth, sibling rank and has-children flag
+int accept_tree(const int32_t *parent, const int32_t *node_rank, int T, int K, int s,
+                AcceptParams &p) {
     if (!parent) return MEDUSA_ERR_NULL;
     if (T < 1 || T > MEDUSA_MAX_TREE) return MEDUSA_ERR_SHAPE;
     if (parent[0] != -1) return MEDUSA_ERR_TREE;
     int depth[MEDUSA_MAX_TREE];
     int nchild[MEDUSA_MAX_TREE] = {0};
+    for (int i = 0; i < MEDUSA_MAX_TREE; ++i) {
+        p.parent[i] = 255;
+        p.rank[i] = p.depth[i] = 0;
+    }
+    for (int i = 0; i < MEDUSA_MAX_TREE / 32; ++i) p.internal[i] = 0u;
     depth[0] = 0;
     for (int n = 1; n < T; ++n) {
         if (parent[n] < 0 || parent[n] >= n) return MEDUSA_ERR_TREE;
@@ -363,6 +451,10 @@ int check_accept_tree(const int32_t *parent, const int32_t *node_rank, int T, in
         const int r = node_rank ? node_rank[n] : nchild[parent[n]];
         if (r < 0 || r >= s) return MEDUSA_ERR_TREE;
         nchild[parent[n]]++;
+        p.parent[n] = (uint8_t)parent[n];
+        p.rank[n] = (uint8_t)r;
+        p.depth[n] = (uint8_t)depth[n];
+        p.internal[parent[n] >> 5] |= 1u << (parent[n] & 31);
     }
     if (node_rank) {
         for (int n = 1; n < T; ++n)
@@ -395,11 +487,16 @@ void accept_chunks(int B, int T, int V, int *nchunk, int *chunk) {
 
 using namespace medusa;
 
-extern "C" size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s) {
-    if (B < 1 || T < 1 || T > MEDUSA_MAX_TREE || V < 1 || K < 0 || s < 1) return 0;
+// workspace: chunk statistics [B][T][nchunk], child logits [B][T], child tokens [B][T]
+static size_t accept_stats_bytes(int B, int T, int V) {
     int nchunk, chunk;
     accept_chunks(B, T, V, &nchunk, &chunk);
     return align_up((size_t)B * T * nchunk * sizeof(RowStat), 256);
+}
+
+extern "C" size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s) {
+    if (B < 1 || T < 1 || T > MEDUSA_MAX_TREE || V < 1 || K < 0 || s < 1) return 0;
+    return accept_stats_bytes(B, T, V) + 2 * align_up((size_t)B * T * sizeof(float), 256);
 }
 
 extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *parent,
@@ -418,15 +515,17 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
         !(temperature > 0.f && temperature < INFINITY && eps > 0.f && eps < INFINITY &&
           delta > 0.f && delta < INFINITY))
         return MEDUSA_ERR_PARAM;
-    const int st = check_accept_tree(parent, node_rank, T, K, s);
+    AcceptParams p;
+    const int st = accept_tree(parent, node_rank, T, K, s, p);
     if (st != MEDUSA_OK) return st;
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < tree_accept_workspace_bytes(B, T, V, K, s))
         return MEDUSA_ERR_WORKSPACE;
 
-    AcceptParams p;
     p.logits = logits;
     p.topk = topk_ids;
     p.stats = (RowStat *)ws;
+    p.childz = (float *)((char *)ws + accept_stats_bytes(B, T, V));
+    p.ctok = (int32_t *)((char *)p.childz + align_up((size_t)B * T * sizeof(float), 256));
     p.accept_len = accept_len;
     p.best_node = best_node;
     p.accepted = accepted_tokens;
@@ -438,14 +537,15 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
     p.K = K;
     p.s = s;
     p.mode = mode;
-    p.has_rank = node_rank != nullptr;
     p.zscale = mode == MEDUSA_TYPICAL ? kLog2e / temperature : 0.f;
     p.eps = eps;
     p.delta = delta;
     accept_chunks(B, T, V, &p.nchunk, &p.chunk);
-    for (int i = 0; i < MEDUSA_MAX_TREE; ++i) {
-        p.parent[i] = i < T && parent[i] >= 0 ? (uint8_t)parent[i] : (uint8_t)255;
-        p.rank[i] = (node_rank && i < T && i > 0) ? (uint8_t)node_rank[i] : (uint8_t)0;
+    {
+        int nleaf = 0;
+        for (int n = 0; n < T; ++n) nleaf += !((p.internal[n >> 5] >> (n & 31)) & 1u);
+        const size_t leaf_bytes = (size_t)B * nleaf * V * (dtype == MEDUSA_BF16 ? 2 : 4);
+        p.leaves = T > 1 && leaf_bytes <= kLeafStatBytes;
     }
     hipStream_t sm = (hipStream_t)stream;
     if (T > 1) {
@@ -457,9 +557,9 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     }
     if (dtype == MEDUSA_BF16)
-        hipLaunchKernelGGL(accept_finish_kernel<bf16_t>, dim3(B), dim3(kThreads), 0, sm, p);
+        hipLaunchKernelGGL(accept_finish_kernel<bf16_t>, dim3(B), dim3(kFinThreads), 0, sm, p);
     else
-        hipLaunchKernelGGL(accept_finish_kernel<float>, dim3(B), dim3(kThreads), 0, sm, p);
+        hipLaunchKernelGGL(accept_finish_kernel<float>, dim3(B), dim3(kFinThreads), 0, sm, p);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

@@ -36,6 +36,14 @@ namespace {
 #endif
 constexpr int kBN = 64;          // keys per LDS stage
 constexpr int kMaxWaves = 8;     // waves per workgroup
+#ifndef MEDUSA_ATTN_MINWG
+#define MEDUSA_ATTN_MINWG 1      // the launch targets one workgroup per CU
+#endif
+#ifndef MEDUSA_ATTN_PD
+#define MEDUSA_ATTN_PD 2
+#endif
+constexpr int kPD = MEDUSA_ATTN_PD;   // stages of K/V loads in flight (1..4; fp32: 1)
+static_assert(kPD >= 1 && kPD <= 4, "prefetch depth 1..4");
 constexpr int kMinChunk = MEDUSA_ATTN_MIN_CHUNK;   // smallest prefix split (keys)
 constexpr int kTargetWG = MEDUSA_ATTN_WG_PER_CU * kNumCU;
 
@@ -254,7 +262,7 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 // NW waves are launched per workgroup; the first p.W of them own query rows,
 // all of them share the staging of K/V.
 template <typename T, int DH, int NW>
-__global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_kernel(AttnParams p) {
     using C = Cfg<T, DH>;
     constexpr int NT = NW * kWave;
     __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
@@ -262,7 +270,6 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    for (int i = tid; i < p.T; i += nthr) par[i] = p.parent[i];
 
     // logical block -> (b, kv head, split, m-tile), m-tile fastest
     const uint32_t lid = xcd_logical_id(blockIdx.x, (uint32_t)p.nwg);
@@ -271,13 +278,35 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
     const int kvh = (int)((lid / ((uint32_t)p.nmt * p.nsplit)) % p.Hkv);
     const int b = (int)(lid / ((uint32_t)p.nmt * p.nsplit * p.Hkv));
 
+    // The prefix length, this lane's query row and the parent table are
+    // loaded together, before the first wait.
+    const int Lraw = p.prefix_len[b];
+    const int col = lane & 31, h = lane >> 5;
+    const int row = mt * 32 * p.W + wave * 32 + col;
+    const bool rvalid = wave < p.W && row < p.M;
+    const int g = rvalid ? row / p.T : 0;
+    const int t = rvalid ? row % p.T : 0;
+    const int hq = kvh * p.G + g;
+    u32x4 qf[C::NKS];
+    {
+        // one resource over the kv head's M query rows (a uniform base: a
+        // per-lane resource would need a loop over the distinct lanes);
+        // lanes without a row read past its end, which returns 0
+        const T *qkv = (const T *)p.q + ((size_t)b * p.Hq + (size_t)kvh * p.G) * p.T * DH;
+        const auto qr = make_rsrc(qkv, (uint32_t)((size_t)p.M * DH * sizeof(T)));
+        const uint32_t qoff = rvalid ? (uint32_t)(((size_t)row * DH + h * C::KC) * sizeof(T)) : 0xFFFFF000u;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+            qf[ks] = buf_ld16(qr, qoff + (uint32_t)(ks * C::KSTEP * sizeof(T)));
+    }
+    for (int i = tid; i < p.T; i += nthr) par[i] = p.parent[i];
+
     if (lid == 0 && tid == 0) {
         int bad = 0;
         for (int i = 0; i < p.B; ++i) bad |= (p.prefix_len[i] < 0 || p.prefix_len[i] > p.Lcap);
         *p.err = bad;
     }
-    int L = p.prefix_len[b];
-    L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+    const int L = Lraw < 0 ? 0 : (Lraw > p.Lcap ? p.Lcap : Lraw);
     const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
     __syncthreads();
     if (p.mask_out && lid == 0) {
@@ -297,21 +326,6 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
     const int kend = kbeg + p.chunk < L ? kbeg + p.chunk : L;
     const bool last = split == nsb - 1;
 
-    // this lane's query row
-    const int col = lane & 31, h = lane >> 5;
-    const int row = mt * 32 * p.W + wave * 32 + col;
-    const bool rvalid = wave < p.W && row < p.M;
-    const int g = rvalid ? row / p.T : 0;
-    const int t = rvalid ? row % p.T : 0;
-    const int hq = kvh * p.G + g;
-
-    u32x4 qf[C::NKS];
-    {
-        const T *qrow = (const T *)p.q + (((size_t)b * p.Hq + hq) * p.T + t) * DH;
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks)
-            qf[ks] = rvalid ? ld16(qrow + ks * C::KSTEP + h * C::KC) : u32x4{0u, 0u, 0u, 0u};
-    }
     uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
     for (int a = t, guard = 0; guard <= p.T; a = par[a], ++guard) {
         const uint64_t bit = 1ull << (a & 63);
@@ -334,11 +348,16 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
     const T *ktb = (const T *)p.kt + ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
     const T *vtb = (const T *)p.vt + ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
     const int npre = (kend - kbeg + kBN - 1) / kBN;
-    const int nstage = npre + (last ? (p.T + kBN - 1) / kBN : 0);
+    const int ntree = p.T;        // the lambdas below take no reference to p:
+    const float cscale = p.c;     // that would copy the parameter block to scratch
+    const int nstage = npre + (last ? (ntree + kBN - 1) / kBN : 0);
     const bool computes = wave < p.W;
 
-    StageCopy<T, DH, NT> cp;
-    auto issue = [&](int sidx) {
+    // PD register sets of staged K/V: the loads of a stage are issued PD
+    // stages before it is written to LDS, so PD stages of bytes are in flight
+    constexpr int PD = sizeof(T) == 2 ? kPD : 1;   // fp32 stages are twice as large
+    StageCopy<T, DH, NT> cp[PD];
+    auto issue = [&](StageCopy<T, DH, NT> &dst, int sidx) __attribute__((always_inline)) {
         const T *kb, *vb;
         int nv;
         if (sidx < npre) {
@@ -348,40 +367,50 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
             vb = vcb + (size_t)k0 * DH;
         } else {
             const int tb = (sidx - npre) * kBN;
-            nv = p.T - tb < kBN ? p.T - tb : kBN;
+            nv = ntree - tb < kBN ? ntree - tb : kBN;
             kb = ktb + (size_t)tb * DH;
             vb = vtb + (size_t)tb * DH;
         }
         const uint32_t nbytes = (uint32_t)(nv * DH * (int)sizeof(T));
-        cp.load(make_rsrc(kb, nbytes), make_rsrc(vb, nbytes), tid);
+        dst.load(make_rsrc(kb, nbytes), make_rsrc(vb, nbytes), tid);
     };
-    // Double-buffered stages, one barrier each: stage i is computed from
-    // buffer i%2 while stage i+1 (loaded during stage i-1) is written to the
-    // other buffer and stage i+2's loads are in flight.
-    issue(0);
-    cp.store(lds[0], tid);
-    if (nstage > 1) issue(1);
+    // Double-buffered LDS stages, one barrier each: stage i is computed from
+    // buffer i%2, then stage i+1 (loads issued PD stages earlier) is written
+    // to the other buffer and the loads of stage i+1+PD go out into the
+    // register set it freed.  The loop is unrolled by PD so that every
+    // register set is named statically.
+    issue(cp[0], 0);
+    cp[0].store(lds[0], tid);
+#pragma unroll
+    for (int k = 1; k <= PD; ++k)
+        if (k < nstage) issue(cp[k % PD], k);
     __syncthreads();
-    for (int sidx = 0; sidx < nstage; ++sidx) {
-        if (computes) {
-            int kind = 0, klim = kBN;
-            uint64_t mword = 0ull;
-            if (sidx < npre) {
-                const int k0 = kbeg + sidx * kBN;
-                klim = kend - k0 < kBN ? kend - k0 : kBN;
-            } else {
-                const int wi = sidx - npre;
-                kind = 1;
-                mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+    for (int base = 0; base < nstage; base += PD) {
+#pragma unroll
+        for (int k = 0; k < PD; ++k) {   // unrolled: register set (k + 1) % PD is static
+            const int sidx = base + k;
+            if (sidx >= nstage) break;
+            if (computes) {
+                int kind = 0, klim = kBN;
+                uint64_t mword = 0ull;
+                if (sidx < npre) {
+                    const int k0 = kbeg + sidx * kBN;
+                    klim = kend - k0 < kBN ? kend - k0 : kBN;
+                } else {
+                    const int wi = sidx - npre;
+                    kind = 1;
+                    mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+                }
+                const bool masked = kind == 1 || klim < kBN;
+                attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword,
+                                    cscale);
             }
-            const bool masked = kind == 1 || klim < kBN;
-            attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword, p.c);
+            if (sidx + 1 < nstage) {
+                cp[(k + 1) % PD].store(lds[(sidx + 1) & 1], tid);
+                if (sidx + 1 + PD < nstage) issue(cp[(k + 1) % PD], sidx + 1 + PD);
+            }
+            __syncthreads();
         }
-        if (sidx + 1 < nstage) {
-            cp.store(lds[(sidx + 1) & 1], tid);
-            if (sidx + 2 < nstage) issue(sidx + 2);
-        }
-        __syncthreads();
     }
 
     const float ltot = st.l + __shfl_xor(st.l, 32);
@@ -418,7 +447,10 @@ __global__ __launch_bounds__(NW *kWave, sizeof(T) == 2 ? 2 : 1) void tree_attn_f
     }
 }
 
-// Merge split partials of the rows whose prefix used more than one split.
+// Merge split partials of the rows whose prefix used more than one split:
+// one wave per row; lane j holds split j's (max, sum) (64 splits per round),
+// then the O partials are read with kCombU splits of loads in flight.
+constexpr int kCombU = 8;
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     const int lane = threadIdx.x % kWave;
@@ -431,18 +463,43 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
     if (nsb == 1) return;
     float mmax = -INFINITY;
-    for (int sp = 0; sp < nsb; ++sp) mmax = fmaxf(mmax, p.part_ml[(size_t)sp * nrows + rowid].x);
+    for (int s0 = 0; s0 < nsb; s0 += kWave) {
+        const float m = s0 + lane < nsb ? p.part_ml[(size_t)(s0 + lane) * nrows + rowid].x : -INFINITY;
+        mmax = fmaxf(mmax, m);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, m));
     constexpr int PER = DH / kWave;
     float acc[PER] = {};
     float den = 0.f;
-    for (int sp = 0; sp < nsb; ++sp) {
-        const float2 ml = p.part_ml[(size_t)sp * nrows + rowid];
-        const float w = fast_exp2(ml.x - mmax);
-        den += w * ml.y;
-        const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH;
+    for (int s0 = 0; s0 < nsb; s0 += kWave) {
+        float w = 0.f;
+        if (s0 + lane < nsb) {
+            const float2 ml = p.part_ml[(size_t)(s0 + lane) * nrows + rowid];
+            w = fast_exp2(ml.x - mmax);
+            den += w * ml.y;
+        }
+        const int n = nsb - s0 < kWave ? nsb - s0 : kWave;
+        for (int j0 = 0; j0 < n; j0 += kCombU) {
+            float v[kCombU][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * src[lane * PER + e];
+            for (int u = 0; u < kCombU; ++u) {
+                const int sp = s0 + (j0 + u < n ? j0 + u : n - 1);   // clamped: weight 0 below
+                const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH + lane * PER;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+            }
+#pragma unroll
+            for (int u = 0; u < kCombU; ++u) {
+                const float wu = __shfl(w, j0 + u < n ? j0 + u : 0);
+                const float wj = j0 + u < n ? wu : 0.f;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += wj * v[u][e];
+            }
+        }
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m);
     const float inv = 1.0f / den;
     T *dst = (T *)p.out + rowid * DH;
 #pragma unroll
