@@ -174,16 +174,22 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # the timed steps run back to back with nothing else on the stream; the
+    # per-call breakdown comes from a second pass of the same steps with an
+    # event between calls (each event costs a little time of its own)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     names = ["heads_stage1", "heads_stage2", "tree_attention", "tree_accept"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in
            enumerate(names)}
