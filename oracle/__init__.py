@@ -157,3 +157,45 @@ def tree_accept(logits, topk_ids, parent, dtype: str, mode: str, temperature: fl
                                   _p(out["ratio"]), _p(out["entropy"]))
     _check(rc, "oracle_tree_accept")
     return out
+
+
+def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, best_node, parent
+                   ) -> Dict[str, np.ndarray]:
+    """Append each sequence's accepted path to its KV cache.
+
+    After acceptance the sequence grows by the root token and the accepted
+    candidates (page "Medusa：基于多Token预测的LLM推理加速", section 3.1, step 4
+    of the decode loop: extend the sequence with the accepted tokens; the
+    aiunderstanding page, section ディープダイブ: the longest matching prefix is
+    kept).  Their keys and values were already computed by the tree pass, so
+    the rows of the path root -> best_node[b] (depth order) are copied to cache
+    positions L_b, L_b + 1, ... and the length advances by the path length.
+    A sequence is left untouched (0 rows written) when L_b is outside
+    [0, Lcap], best_node[b] is outside [0, T) or the path does not fit.
+    Works on the stored element bits (any dtype): a pure copy.
+    """
+    k_cache, v_cache = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    L = _c(prefix_len, np.int32).copy()
+    best_node = _c(best_node, np.int32)
+    parent = _c(parent, np.int32)
+    B, Hkv, Lcap, _ = k_cache.shape
+    T = parent.shape[0]
+    committed = np.zeros(B, np.int32)
+    for b in range(B):
+        best = int(best_node[b])
+        if not (0 <= L[b] <= Lcap) or not (0 <= best < T):
+            continue
+        path = []
+        a = best
+        while a != -1:
+            path.append(a)
+            a = int(parent[a])
+        path.reverse()                      # root first
+        if L[b] + len(path) > Lcap:
+            continue
+        for j, node in enumerate(path):
+            k_cache[b, :, L[b] + j, :] = k_tree[b, :, node, :]
+            v_cache[b, :, L[b] + j, :] = v_tree[b, :, node, :]
+        committed[b] = len(path)
+        L[b] += len(path)
+    return {"k_cache": k_cache, "v_cache": v_cache, "prefix_len": L, "committed": committed}

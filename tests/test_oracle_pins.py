@@ -396,3 +396,62 @@ def test_typical_workload_entropy_spread(name):
     r = o["ratio"][:, 1:]
     assert np.all(np.abs(r - 1) > 1e-3)
     assert 0 < o["accept_len"].mean() < wl.K
+
+
+# ------------------------------------------------------- KV commit (next row f1)
+def _kv(B, Hkv, L, T, dh, seed):
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(0, 60000, (B, Hkv, L, dh)).astype(np.uint16)
+    vc = rng.integers(0, 60000, (B, Hkv, L, dh)).astype(np.uint16)
+    kt = rng.integers(0, 60000, (B, Hkv, T, dh)).astype(np.uint16)
+    vt = rng.integers(0, 60000, (B, Hkv, T, dh)).astype(np.uint16)
+    return kc, vc, kt, vt
+
+
+def test_commit_chain_tree_copies_rows_in_order():
+    """A chain tree accepted to its tip appends every tree row, in order."""
+    kc, vc, kt, vt = _kv(1, 2, 16, 4, 8, 1)
+    o = oracle.tree_commit_kv(kc, vc, [5], kt, vt, [3], [-1, 0, 1, 2])
+    assert o["committed"].tolist() == [4] and o["prefix_len"].tolist() == [9]
+    np.testing.assert_array_equal(o["k_cache"][0, :, 5:9], kt[0])
+    np.testing.assert_array_equal(o["v_cache"][0, :, 5:9], vt[0])
+    # everything else is untouched
+    np.testing.assert_array_equal(o["k_cache"][0, :, :5], kc[0, :, :5])
+    np.testing.assert_array_equal(o["k_cache"][0, :, 9:], kc[0, :, 9:])
+
+
+def test_commit_branching_path_by_hand():
+    """Full 2x2 tree (parents -1,0,0,1,1,2,2): node 6's path is 0 -> 2 -> 6."""
+    kc, vc, kt, vt = _kv(2, 1, 8, 7, 4, 2)
+    parent = [-1, 0, 0, 1, 1, 2, 2]
+    o = oracle.tree_commit_kv(kc, vc, [0, 6], kt, vt, [6, 0], parent)
+    assert o["committed"].tolist() == [3, 1] and o["prefix_len"].tolist() == [3, 7]
+    np.testing.assert_array_equal(o["k_cache"][0, 0, 0:3], kt[0, 0, [0, 2, 6]])
+    np.testing.assert_array_equal(o["v_cache"][0, 0, 0:3], vt[0, 0, [0, 2, 6]])
+    np.testing.assert_array_equal(o["k_cache"][1, 0, 6], kt[1, 0, 0])   # root only
+    np.testing.assert_array_equal(o["k_cache"][1, 0, :6], kc[1, 0, :6])
+
+
+def test_commit_rejections_leave_the_cache_alone():
+    """No room, a length outside [0, Lcap] or a best node outside [0, T):
+    nothing is written and the length stays."""
+    kc, vc, kt, vt = _kv(4, 1, 8, 3, 4, 3)
+    parent = [-1, 0, 1]
+    o = oracle.tree_commit_kv(kc, vc, [6, 9, -1, 2], kt, vt, [2, 0, 0, 3], parent)
+    assert o["committed"].tolist() == [0, 0, 0, 0]
+    assert o["prefix_len"].tolist() == [6, 9, -1, 2]
+    np.testing.assert_array_equal(o["k_cache"], kc)
+    np.testing.assert_array_equal(o["v_cache"], vc)
+    # exactly full: L + path = Lcap fits
+    o = oracle.tree_commit_kv(kc, vc, [5, 0, 0, 0], kt, vt, [2, 0, 0, 0], parent)
+    assert o["committed"].tolist() == [3, 1, 1, 1] and o["prefix_len"][0] == 8
+
+
+def test_commit_length_is_depth_plus_one():
+    """Rows written = depth(best) + 1 (depth from the C tree oracle)."""
+    t = W.pruned_tree(W.WORKLOADS["llama7b_b1"].rates, 3, 64)
+    dep = oracle.tree(t.parent, 4, 3)["depth"]
+    kc, vc, kt, vt = _kv(1, 1, 64, t.T, 2, 4)
+    for best in range(t.T):
+        o = oracle.tree_commit_kv(kc, vc, [10], kt, vt, [best], t.parent)
+        assert o["committed"][0] == dep[best] + 1
