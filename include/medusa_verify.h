@@ -12,6 +12,7 @@
  *   tree_attention     every tree node attends to the KV prefix plus its own
  *                      ancestors (and itself) -- one pass over the tree
  *   tree_accept        greedy or typical acceptance of the longest valid path
+ *   tree_commit_kv     append the accepted path's K/V rows to the cache
  *
  * Conventions (all calls):
  *  - Every pointer marked "device" is device memory on the current HIP
@@ -184,6 +185,36 @@ int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *pare
                 int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
 
 size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s);
+
+/* ------------------------------------------------------------------------
+ * tree_commit_kv -- append the accepted path's keys and values to the cache.
+ *
+ * The step after acceptance: the sequence grows by the root token and the
+ * accepted candidates (page "Medusa：基于多Token预测的LLM推理加速", section 3.1,
+ * step 4 of the decode loop; aiunderstanding page, section ディープダイブ: the
+ * longest matching prefix is kept).  Their K/V rows already exist from the
+ * tree pass: for each sequence b the rows of the nodes on the path
+ * root -> best_node[b], in depth order, are copied to cache positions
+ * prefix_len[b], prefix_len[b] + 1, ..., and prefix_len[b] advances by the
+ * path length (depth(best) + 1 = accept_len + 1 rows).
+ *
+ *   k_cache, v_cache device [B][Hkv][Lcap][dh] dtype, updated in place
+ *   prefix_len       device [B] int32, advanced in place
+ *   k_tree, v_tree   device [B][Hkv][T][dh] dtype (as tree_attention)
+ *   best_node        device [B] int32 (as written by tree_accept)
+ *   parent           host [T] int32 (as tree_attention)
+ *   committed        device [B] int32 or NULL: rows written for b; 0 when
+ *                    the sequence was left untouched because prefix_len[b]
+ *                    is outside [0, Lcap], best_node[b] is outside [0, T)
+ *                    or the path does not fit below Lcap
+ *
+ * Limits: 1 <= T <= 256, dh * element size a multiple of 16 bytes.  A pure
+ * copy (bit-exact).  Needs no workspace.
+ * ---------------------------------------------------------------------- */
+int tree_commit_kv(void *k_cache, void *v_cache, int32_t *prefix_len, const void *k_tree,
+                   const void *v_tree, const int32_t *best_node, const int32_t *parent, int B,
+                   int Hkv, int Lcap, int dh, int T, int dtype, int32_t *committed,
+                   void *stream);
 
 /* Text for a medusa_status value (static storage). */
 const char *medusa_status_str(int status);

@@ -27,7 +27,8 @@ STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "ME
 
 EXPORTS = ["medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2",
            "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
-           "tree_accept", "tree_accept_workspace_bytes", "medusa_status_str", "medusa_abi_version"]
+           "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_status_str",
+           "medusa_abi_version"]
 
 
 class MedusaError(RuntimeError):
@@ -53,11 +54,12 @@ def _load() -> ctypes.CDLL:
     L.tree_accept.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, F, F, P, P, P, P, P, P, Z, P]
     L.tree_accept_workspace_bytes.argtypes = [I, I, I, I, I]
     L.tree_accept_workspace_bytes.restype = Z
+    L.tree_commit_kv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
     for f in ("medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2", "tree_attention",
-              "tree_accept"):
+              "tree_accept", "tree_commit_kv"):
         getattr(L, f).restype = I
     return L
 
@@ -199,3 +201,21 @@ def tree_accept(logits, topk_ids, parent, mode: int, temperature: float = 1.0, e
                          ws.numel(), _stream(stream))
     _check("tree_accept", rc)
     return out
+
+
+def tree_commit_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: torch.Tensor,
+                   k_tree: torch.Tensor, v_tree: torch.Tensor, best_node: torch.Tensor, parent,
+                   committed: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """Append the accepted path's K/V rows to the caches (in place) and
+    advance prefix_len (in place); returns `committed` if given."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (prefix_len, "prefix_len"),
+                 (k_tree, "k_tree"), (v_tree, "v_tree"), (best_node, "best_node")):
+        _need(t, n)
+    B, Hkv, Lcap, dh = k_cache.shape
+    T = k_tree.shape[2]
+    par, par_p = _host_i32(parent)
+    rc = lib.tree_commit_kv(_ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(k_tree),
+                            _ptr(v_tree), _ptr(best_node), par_p, B, Hkv, Lcap, dh, T,
+                            _dtype_code(k_cache), _ptr(committed), _stream(stream))
+    _check("tree_commit_kv", rc)
+    return committed

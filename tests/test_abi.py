@@ -119,3 +119,19 @@ def test_accept_validation(mv):
     assert call(rank=_i32([0, 0, 5, 0])) == -4                # rank >= s
     assert call(T=257) == -2
     assert call(ws=None) == -5 and call(wsb=0) == -5
+
+
+def test_commit_validation(mv):
+    L = mv.lib
+    par = _i32([-1, 0, 0, 1])
+
+    def call(kc=FAKE, parent=par, B=2, Hkv=2, Lcap=64, dh=128, T=4, dt=1):
+        return L.tree_commit_kv(kc, FAKE, FAKE, FAKE, FAKE, FAKE, parent, B, Hkv, Lcap, dh, T, dt,
+                                None, None)
+    assert call(kc=None) == -1 and call(parent=None) == -1
+    assert call(dt=2) == -3
+    assert call(B=0) == -2 and call(Hkv=0) == -2 and call(Lcap=-1) == -2
+    assert call(dh=12) == -2                                  # 24 bytes: not a 16-byte multiple
+    assert call(dt=0, dh=6) == -2 and call(T=0) == -2 and call(T=257) == -2
+    assert call(parent=_i32([0, 0, 0, 1])) == -4              # root must be -1
+    assert call(parent=_i32([-1, 0, 2, 1])) == -4             # parent[n] < n
