@@ -19,7 +19,7 @@ _SRC = os.path.join(_HERE, "medusa_oracle.c")
 _LIB = os.path.join(_HERE, "libmedusa_oracle.so")
 
 DTYPE_CODE = {"f32": 0, "bf16": 1}
-MODE_CODE = {"greedy": 0, "typical": 1}
+MODE_CODE = {"greedy": 0, "typical": 1, "typical_loglik": 2}
 
 _lib = None
 
@@ -47,7 +47,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_tree.argtypes = [P, P, I, I, I, P, P, P]
         L.oracle_tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P, I, P]
         L.oracle_tree_accept.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, D, D,
-                                         P, P, P, P, P, P, P, P]
+                                         P, P, P, P, P, P, P, P, P]
         L.oracle_num_threads.argtypes = []
         for f in ("oracle_heads_topk", "oracle_tree", "oracle_tree_attention",
                   "oracle_tree_accept", "oracle_num_threads"):
@@ -148,13 +148,14 @@ def tree_accept(logits, topk_ids, parent, dtype: str, mode: str, temperature: fl
         "valid": np.empty((B, T), np.uint8),
         "ratio": np.empty((B, T), np.float64),
         "entropy": np.empty((B, T), np.float64),
+        "score": np.empty((B, T), np.float64),
     }
     rc = lib().oracle_tree_accept(_p(logits), _p(topk_ids), _p(parent), _p(nr), B, T, V, K, s,
                                   DTYPE_CODE[dtype], MODE_CODE[mode], float(temperature),
                                   float(eps), float(delta), _p(out["accept_len"]),
                                   _p(out["best_node"]), _p(out["accepted_tokens"]),
                                   _p(out["node_tokens"]), _p(out["next_token"]), _p(out["valid"]),
-                                  _p(out["ratio"]), _p(out["entropy"]))
+                                  _p(out["ratio"]), _p(out["entropy"]), _p(out["score"]))
     _check(rc, "oracle_tree_accept")
     return out
 
@@ -199,3 +200,35 @@ def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, best_node, pare
         committed[b] = len(path)
         L[b] += len(path)
     return {"k_cache": k_cache, "v_cache": v_cache, "prefix_len": L, "committed": committed}
+
+
+def sample_token(logits, rows, u, temperature: float, dtype: str) -> Dict[str, np.ndarray]:
+    """The bonus token drawn from p = softmax(logits[b][rows[b]] / temperature)
+    by inversion of its distribution function with the caller's uniform
+    u[b] in [0, 1): the first token t whose cumulative probability
+    P(<= t) exceeds u (page "Medusa：基于多Token预测的LLM推理加速", section 3.3:
+    sampled verification draws from the tempered softmax).  fp64 throughout.
+    Also returns, per sequence, P(< t) and P(<= t) of the drawn token; rows
+    outside [0, T) or u outside [0, 1) give token -1."""
+    logits = _stored(logits, dtype)
+    x = logits.astype(np.float32) if dtype == "f32" else \
+        (logits.astype(np.uint32) << 16).view(np.float32)
+    rows = _c(rows, np.int32)
+    u = np.asarray(u, np.float64)
+    B, T, V = x.shape
+    tok = np.full(B, -1, np.int32)
+    lo = np.zeros(B)
+    hi = np.zeros(B)
+    for b in range(B):
+        r = int(rows[b])
+        if not (0 <= r < T) or not (0.0 <= u[b] < 1.0):
+            continue
+        z = x[b, r].astype(np.float64) / temperature
+        p = np.exp(z - z.max())
+        cdf = np.cumsum(p) / p.sum()
+        t = int(np.searchsorted(cdf, u[b], side="right"))   # first t with cdf[t] > u
+        t = min(t, V - 1)
+        tok[b] = t
+        lo[b] = cdf[t - 1] if t > 0 else 0.0
+        hi[b] = cdf[t]
+    return {"token": tok, "cdf_lo": lo, "cdf_hi": hi}

@@ -340,13 +340,13 @@ int oracle_tree_accept(const void *logits, const int32_t *topk_ids, const int32_
                        int mode, double temperature, double eps, double delta,
                        int32_t *accept_len, int32_t *best_node, int32_t *accepted_tokens,
                        int32_t *node_tokens, int32_t *next_token, uint8_t *valid_out,
-                       double *ratio_out, double *entropy_out)
+                       double *ratio_out, double *entropy_out, double *score_out)
 {
     if (!logits || !topk_ids || !parent || !accept_len || !best_node || !accepted_tokens ||
         B < 1 || T < 1 || V < 1 || K < 0 || s < 1 || (dtype != 0 && dtype != 1) ||
-        (mode != 0 && mode != 1))
+        (mode != 0 && mode != 1 && mode != 2))
         return OR_ERR_ARG;
-    if (mode == 1 && !(temperature > 0.0))
+    if (mode != 0 && !(temperature > 0.0))
         return OR_ERR_ARG;
     int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * T);
     int32_t *rank = (int32_t *)malloc(sizeof(int32_t) * T);
@@ -362,7 +362,9 @@ int oracle_tree_accept(const void *logits, const int32_t *topk_ids, const int32_
         int32_t *tok = (int32_t *)malloc(sizeof(int32_t) * T);
         uint8_t *valid = (uint8_t *)malloc(T);
         double *prob = (double *)malloc(sizeof(double) * V);
+        double *lp = (double *)malloc(sizeof(double) * T);   /* ln p of each node's token */
         tok[0] = -1;
+        for (int n = 0; n < T; ++n) lp[n] = 0.0;
         for (int n = 1; n < T; ++n)
             tok[n] = topk_ids[((size_t)b * K + depth[n] - 1) * s + rank[n]];
         valid[0] = 1;
@@ -409,20 +411,30 @@ int oracle_tree_accept(const void *logits, const int32_t *topk_ids, const int32_
                     if (parent[c] == p) {
                         double pc = (tok[c] >= 0 && tok[c] < V) ? prob[tok[c]] : 0.0;
                         valid[c] = pc > thr;
+                        lp[c] = pc > 0.0 ? log(pc) : -INFINITY;
                         if (ratio_out) ratio_out[(size_t)b * T + c] = pc / thr;
                     }
             }
         }
 
-        /* longest valid path: walk every node up to the root */
+        /* longest valid path: walk every node up to the root.  Equal depths:
+           mode 2 prefers the larger path log-likelihood (sum of ln p of the
+           path's tokens), then the lower index; modes 0 and 1 the lower index. */
         int best = 0, best_d = 0;
+        double best_s = 0.0;
+        if (score_out) score_out[(size_t)b * T] = 0.0;
         for (int n = 1; n < T; ++n) {
             int ok = 1;
-            for (int a = n; a > 0; a = parent[a])
+            double sc = 0.0;
+            for (int a = n; a > 0; a = parent[a]) {
                 if (!valid[a]) ok = 0;
-            if (ok && depth[n] > best_d) {
+                sc += lp[a];
+            }
+            if (score_out) score_out[(size_t)b * T + n] = sc;
+            if (ok && (depth[n] > best_d || (mode == 2 && depth[n] == best_d && sc > best_s))) {
                 best = n;
                 best_d = depth[n];
+                best_s = sc;
             }
         }
         accept_len[b] = best_d;
@@ -445,6 +457,7 @@ int oracle_tree_accept(const void *logits, const int32_t *topk_ids, const int32_
         free(tok);
         free(valid);
         free(prob);
+        free(lp);
     }
     free(depth);
     free(rank);

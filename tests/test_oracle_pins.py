@@ -455,3 +455,94 @@ def test_commit_length_is_depth_plus_one():
     for best in range(t.T):
         o = oracle.tree_commit_kv(kc, vc, [10], kt, vt, [best], t.parent)
         assert o["committed"][0] == dep[best] + 1
+
+
+# ------------------------------------------------------- typical variants (next row f3)
+def test_loglik_tiebreak_by_hand():
+    """Two valid depth-1 children of the root: typical mode keeps the lower
+    index, the log-likelihood variant the more probable token."""
+    parent = [-1, 0, 0]
+    ids = np.array([[[3, 5]]], np.int32)          # node 1 -> token 3, node 2 -> token 5
+    logits = np.zeros((1, 3, 8), np.float32)
+    logits[0, 0, 3], logits[0, 0, 5] = 2.0, 3.0   # both well above the threshold
+    a = oracle.tree_accept(logits, ids, parent, "f32", "typical")
+    b = oracle.tree_accept(logits, ids, parent, "f32", "typical_loglik")
+    assert a["best_node"][0] == 1 and b["best_node"][0] == 2
+    assert a["accept_len"][0] == b["accept_len"][0] == 1
+    # the score is ln p of the token under softmax(row): closed form
+    p5 = np.exp(3.0) / (np.exp(2.0) + np.exp(3.0) + 6.0)
+    assert abs(b["score"][0, 2] - np.log(p5)) < 1e-12
+    # equal scores: the lower index wins in both modes
+    logits[0, 0, 5] = 2.0
+    b = oracle.tree_accept(logits, ids, parent, "f32", "typical_loglik")
+    assert b["best_node"][0] == 1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_loglik_matches_path_enumeration(seed):
+    """Brute force: among the deepest all-valid paths, the one whose summed
+    log-softmax probability (scipy's log_softmax) is largest."""
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(100 + seed)
+    t = W.random_tree(seed, 20, 3, 3)
+    V, tau = 12, 0.8
+    ids = np.stack([rng.permutation(V)[:3] for _ in range(3)])[None].astype(np.int32)
+    logits = (rng.standard_normal((1, t.T, V)) * 2).astype(np.float32)
+    o = oracle.tree_accept(logits, ids, t.parent, "f32", "typical_loglik", temperature=tau)
+    dep = oracle.tree(t.parent, 3, 3)["depth"]
+    tok = o["node_tokens"][0]
+    lsm = log_softmax(logits[0].astype(np.float64) / tau, axis=-1)
+    best, key = 0, (0, 0.0)
+    for n in range(1, t.T):
+        path = []
+        a = n
+        while a > 0:
+            path.append(a)
+            a = t.parent[a]
+        if all(o["valid"][0][a] for a in path):
+            sc = sum(lsm[t.parent[a], tok[a]] for a in path)
+            if (dep[n], sc) > key:
+                best, key = n, (dep[n], sc)
+    assert o["best_node"][0] == best
+    assert o["accept_len"][0] == dep[best]
+
+
+def test_sample_special_cases():
+    V = 10
+    x = np.zeros((3, 2, V), np.float32)
+    x[0, 1, 7] = 60.0                                  # one-hot in effect
+    o = oracle.sample_token(x, [1, 0, 0], [0.99, 0.0, 1 - 1e-12], 1.0, "f32")
+    assert o["token"].tolist() == [7, 0, V - 1]        # u = 0 -> first, u -> 1 -> last
+    # uniform rows: token = floor(u * V)
+    us = np.linspace(0.0, 0.999, 37)
+    for uu in us:
+        o = oracle.sample_token(np.zeros((1, 1, V), np.float32), [0], [uu], 0.7, "f32")
+        assert o["token"][0] == int(np.floor(uu * V + 1e-9))
+    # invalid row or u -> -1
+    o = oracle.sample_token(x, [2, 0, -1], [0.5, 1.0, 0.5], 1.0, "f32")
+    assert o["token"].tolist() == [-1, -1, -1]
+
+
+def test_sample_stratified_counts_match_softmax():
+    """With the stratified uniforms (k + 1/2) / N every token is drawn
+    floor or ceil of N p times (inversion of the distribution function)."""
+    rng = np.random.default_rng(3)
+    V, N, tau = 9, 2000, 0.6
+    row = rng.standard_normal(V).astype(np.float32)
+    x = np.broadcast_to(row, (N, 1, V)).copy()
+    u = (np.arange(N) + 0.5) / N
+    tok = oracle.sample_token(x, np.zeros(N, np.int32), u, tau, "f32")["token"]
+    p = np.exp(row / tau - (row / tau).max())
+    p /= p.sum()
+    cnt = np.bincount(tok, minlength=V)
+    assert np.all(np.abs(cnt - N * p) <= 1.0 + 1e-9), (cnt, N * p)
+
+
+def test_sample_temperature_is_a_logit_scale():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 3, 50)).astype(np.float32)
+    u = rng.random(5)
+    a = oracle.sample_token(x, [0, 1, 2, 0, 1], u, 0.5, "f32")["token"]
+    b = oracle.sample_token((x / np.float32(0.5)).astype(np.float32), [0, 1, 2, 0, 1], u, 1.0,
+                            "f32")["token"]
+    np.testing.assert_array_equal(a, b)
