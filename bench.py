@@ -230,10 +230,44 @@ def main():
         "stages": stages,
     }
 
+    result["next_rows"] = {"kv_commit": measure_commit(mv, wl, tree, kc, vc, kt, vt, plen,
+                                                       acc["best_node"], args.steps)}
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, hx, ax, tree, cand, vlog_np, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
     print(json.dumps(result), flush=True)
+
+
+def measure_commit(mv, wl, tree, kc, vc, kt, vt, plen, best_node, steps):
+    """The accepted-path KV commit (the step after acceptance) on its own: the
+    caches get T rows of spare capacity, the lengths are reset before every
+    call (outside the timed interval) and each call is bracketed by events."""
+    import torch
+    B, Hkv, Lcap, dh = kc.shape
+    kc2 = torch.zeros((B, Hkv, Lcap + wl.T, dh), dtype=kc.dtype, device=kc.device)
+    vc2 = torch.zeros_like(kc2)
+    kc2[:, :, :Lcap].copy_(kc)
+    vc2[:, :, :Lcap].copy_(vc)
+    lens = plen.clone()
+    com = torch.empty(B, dtype=torch.int32, device=kc.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps + 3):
+        lens.copy_(plen)
+        e = ev[i - 3] if i >= 3 else None
+        if e:
+            e[0].record()
+        mv.tree_commit_kv(kc2, vc2, lens, kt, vt, best_node, tree.parent, committed=com)
+        if e:
+            e[1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    rows = int(com.sum().item())
+    w = kc.element_size()
+    nbytes = 2 * 2 * Hkv * rows * dh * w          # K and V rows: read from the tree, written to the cache
+    return {"us": round(us, 2), "rows": rows, "bytes": nbytes,
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 2)}
 
 
 def cpu_baseline(wl, hx, ax, tree, cand, vlog_np, budget_s):

@@ -12,6 +12,7 @@
  *   tree_attention     every tree node attends to the KV prefix plus its own
  *                      ancestors (and itself) -- one pass over the tree
  *   tree_accept        greedy or typical acceptance of the longest valid path
+ *   medusa_sample_token a sampled bonus token from the best node's row
  *   tree_commit_kv     append the accepted path's K/V rows to the cache
  *
  * Conventions (all calls):
@@ -46,7 +47,11 @@ extern "C" {
 
 typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
 
-typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_accept_mode;
+typedef enum {
+    MEDUSA_GREEDY = 0,
+    MEDUSA_TYPICAL = 1,
+    MEDUSA_TYPICAL_LOGLIK = 2   /* typical; equal-depth paths ranked by log-likelihood */
+} medusa_accept_mode;
 
 typedef enum {
     MEDUSA_OK = 0,
@@ -160,9 +165,15 @@ size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int dh, 
  *                  valid iff p(tok) > min(eps, delta * exp(-H)) (same
  *                  section's inequality; its defaults eps = 0.09,
  *                  delta = 0.6).
+ *   MEDUSA_TYPICAL_LOGLIK  as MEDUSA_TYPICAL; among equally deep valid
+ *                  paths the one with the largest sum of ln p(tok) over its
+ *                  nodes wins (page "Medusa：基于多Token预测的LLM推理加速",
+ *                  section 5.3: its verification result carries such a
+ *                  log-probability sum), then the lowest node index.
+ *                  Scores are fp32.
  * The accepted path ends at the deepest node whose path from the root is
  * all valid (the first rejection ends a path); equal depths -> lowest
- * node index.
+ * node index (MEDUSA_GREEDY, MEDUSA_TYPICAL).
  *
  *   logits          device [B][T][V] dtype (the base model's logits at every
  *                   tree node)
@@ -175,8 +186,8 @@ size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int dh, 
  *   node_tokens     device [B][T] int32 or NULL: tok(n), root = -1
  *   next_token      device [B] int32 or NULL: argmax of logits[b][best_node]
  *
- * Limits: T <= 256, depth <= K <= 16, rank < s <= 255, V >= 1; typical
- * mode needs temperature > 0, 0 < eps, 0 < delta.
+ * Limits: T <= 256, depth <= K <= 16, rank < s <= 255, V >= 1; the typical
+ * modes need temperature > 0, 0 < eps, 0 < delta.
  * ---------------------------------------------------------------------- */
 int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *parent,
                 const int32_t *node_rank, int B, int T, int V, int K, int s, int dtype, int mode,
@@ -185,6 +196,32 @@ int tree_accept(const void *logits, const int32_t *topk_ids, const int32_t *pare
                 int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
 
 size_t tree_accept_workspace_bytes(int B, int T, int V, int K, int s);
+
+/* ------------------------------------------------------------------------
+ * medusa_sample_token -- a sampled bonus token from the best node's row.
+ *
+ * Sampled verification draws from p = softmax(row / temperature) (page
+ * "Medusa：基于多Token预测的LLM推理加速", section 3.3; at temperature 0 it is
+ * the argmax, which tree_accept's next_token already gives).  The draw is
+ * the inversion of p's distribution function with a caller-supplied uniform:
+ * token[b] is the first t whose cumulative probability P(<= t) exceeds
+ * u[b].  The caller owns the random numbers, so equal inputs give equal
+ * tokens.
+ *
+ *   logits  device [B][T][V] dtype (as tree_accept)
+ *   rows    device [B] int32: the row of each sequence (e.g. tree_accept's
+ *           best_node)
+ *   u       device [B] float32 uniforms in [0, 1)
+ *   token   device [B] int32: the drawn token; -1 when rows[b] is outside
+ *           [0, T) or u[b] outside [0, 1)
+ *
+ * Arithmetic: fp32 (exp2 of the row minus its maximum, sums in a fixed
+ * order), so a u within about 1e-6 of a cumulative boundary can land on
+ * either neighbour.  Rows need at least one finite logit.  Limits: V >= 1,
+ * temperature > 0.  Needs no workspace.
+ * ---------------------------------------------------------------------- */
+int medusa_sample_token(const void *logits, const int32_t *rows, const float *u, int B, int T,
+                        int V, int dtype, float temperature, int32_t *token, void *stream);
 
 /* ------------------------------------------------------------------------
  * tree_commit_kv -- append the accepted path's keys and values to the cache.

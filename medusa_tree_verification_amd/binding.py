@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmedusa_verify.so")
 
 F32, BF16 = 0, 1
-GREEDY, TYPICAL = 0, 1
+GREEDY, TYPICAL, TYPICAL_LOGLIK = 0, 1, 2
 
 STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "MEDUSA_ERR_DTYPE",
           -4: "MEDUSA_ERR_TREE", -5: "MEDUSA_ERR_WORKSPACE", -6: "MEDUSA_ERR_PARAM",
@@ -27,7 +27,8 @@ STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "ME
 
 EXPORTS = ["medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2",
            "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
-           "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_status_str",
+           "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
+           "medusa_status_str",
            "medusa_abi_version"]
 
 
@@ -55,11 +56,12 @@ def _load() -> ctypes.CDLL:
     L.tree_accept_workspace_bytes.argtypes = [I, I, I, I, I]
     L.tree_accept_workspace_bytes.restype = Z
     L.tree_commit_kv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+    L.medusa_sample_token.argtypes = [P, P, P, I, I, I, I, F, P, P]
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
     for f in ("medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2", "tree_attention",
-              "tree_accept", "tree_commit_kv"):
+              "tree_accept", "tree_commit_kv", "medusa_sample_token"):
         getattr(L, f).restype = I
     return L
 
@@ -219,3 +221,19 @@ def tree_commit_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_len: tor
                             _dtype_code(k_cache), _ptr(committed), _stream(stream))
     _check("tree_commit_kv", rc)
     return committed
+
+
+def medusa_sample_token(logits: torch.Tensor, rows: torch.Tensor, u: torch.Tensor,
+                        temperature: float, token: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Bonus token per sequence drawn from softmax(logits[b][rows[b]] / temperature)
+    by inversion with the uniforms u (device float32 [B])."""
+    for t, n in ((logits, "logits"), (rows, "rows"), (u, "u")):
+        _need(t, n)
+    B, T, V = logits.shape
+    if token is None:
+        token = torch.empty(B, dtype=torch.int32, device=logits.device)
+    rc = lib.medusa_sample_token(_ptr(logits), _ptr(rows), _ptr(u), B, T, V, _dtype_code(logits),
+                                 float(temperature), _ptr(token), _stream(stream))
+    _check("medusa_sample_token", rc)
+    return token

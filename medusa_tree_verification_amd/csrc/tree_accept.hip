@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) 
 
     const int lo = j * p.chunk;
     const int hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
-    const bool typical = p.mode == MEDUSA_TYPICAL;
+    const bool typical = p.mode != MEDUSA_GREEDY;
     const T *row = (const T *)p.logits + ((size_t)b * p.T + n) * p.V;
     // thread c looks up node c's token (loads issued unconditionally, before
     // the row pass, so that their latency hides under it)
@@ -278,11 +278,12 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AcceptParams
     __shared__ RowStat sst[kMaxStats];        // this sequence's chunk statistics
     __shared__ int marg[MEDUSA_MAX_TREE];     // merged, per internal node
     __shared__ float mm[MEDUSA_MAX_TREE], mS[MEDUSA_MAX_TREE], mthr[MEDUSA_MAX_TREE];
-    __shared__ int keys[kFinThreads / kWave];
+    __shared__ float lp[MEDUSA_MAX_TREE];     // ln p of every node's token (log-likelihood mode)
+    __shared__ unsigned long long keys[kFinThreads / kWave];
     __shared__ ArgMax red[kFinThreads / kWave];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const bool typical = p.mode == MEDUSA_TYPICAL;
+    const bool typical = p.mode != MEDUSA_GREEDY;
 
     // global loads, issued before any wait: the per-node tables, tokens and
     // child logits, then the chunk statistics (every record of the sequence;
@@ -372,36 +373,58 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AcceptParams
         if (c > 0) {
             const int pn = par[c];
             const int tok = ntok[c];
-            if (!typical)
+            float l = -INFINITY;
+            if (!typical) {
                 ok = tok == marg[pn];
-            else if (tok >= 0 && tok < p.V)
-                ok = exp2f(cz[c] * p.zscale - mm[pn]) / mS[pn] > mthr[pn];
-            else
+            } else if (tok >= 0 && tok < p.V) {
+                const float d = cz[c] * p.zscale - mm[pn];   // log2 units
+                ok = exp2f(d) / mS[pn] > mthr[pn];
+                l = d * kLn2 - logf(mS[pn]);                 // ln p(tok)
+            } else {
                 ok = false;
+            }
+            lp[c] = l;
+        } else {
+            lp[c] = 0.f;
         }
         valid[c] = ok;
     }
     __syncthreads();
 
-    // deepest node whose path is all valid: key (depth << 16) | (0xFFFF - node)
-    int key = -1;
+    // deepest node whose path is all valid; equal depths: the larger path
+    // log-likelihood in log-likelihood mode, then the lower index.  Key:
+    // depth (bits 56..63) | order-preserving bits of the score (24..55) |
+    // 0xFFFF - node (0..15); 0 marks "not valid" (every valid key is > 0).
+    unsigned long long key = 0ull;
     if (tid < p.T) {
         const int n = tid;
         bool ok = true;
-        for (int a = n, g = 0; a != 0 && g <= p.T; a = par[a], ++g) ok = ok && valid[a] != 0;
-        if (ok) key = ((int)dep[n] << 16) | (0xFFFF - n);
+        float sc = 0.f;
+        for (int a = n, g = 0; a != 0 && g <= p.T; a = par[a], ++g) {
+            ok = ok && valid[a] != 0;
+            sc += lp[a];
+        }
+        if (ok) {
+            uint32_t ord = 0u;
+            if (p.mode == MEDUSA_TYPICAL_LOGLIK) {
+                const uint32_t u = __float_as_uint(sc);
+                ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // monotone in sc
+            }
+            key = ((unsigned long long)dep[n] << 56) | ((unsigned long long)ord << 24) |
+                  (unsigned long long)(0xFFFF - n);
+        }
         if (p.node_tokens) p.node_tokens[(size_t)b * p.T + n] = ntok[n];
     }
     for (int m = 32; m >= 1; m >>= 1) {
-        const int o = __shfl_xor(key, m);
+        const unsigned long long o = __shfl_xor(key, m);
         key = o > key ? o : key;
     }
     const int lane = tid % kWave, wave = tid / kWave;
     if (lane == 0) keys[wave] = key;
     __syncthreads();
-    int best_key = keys[0];
+    unsigned long long best_key = keys[0];
     for (int w = 1; w < kFinThreads / kWave; ++w) best_key = keys[w] > best_key ? keys[w] : best_key;
-    const int best = 0xFFFF - (best_key & 0xFFFF);
+    const int best = 0xFFFF - (int)(best_key & 0xFFFFull);
     const int bdep = dep[best];
     if (tid == 0) {
         p.accept_len[b] = bdep;
@@ -427,6 +450,125 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AcceptParams
     row_stats<T, kScanUnroll, kFinThreads>(row, 0, p.V, p.V, false, 0.f, am, unused);
     const ArgMax r = block_argmax<kFinThreads>(am, red);
     if (tid == 0) p.next_token[b] = r.i;
+}
+
+// ---------------------------------------------------------------- bonus token
+// The bonus token drawn from p = softmax(logits[b][rows[b]] / temperature)
+// (page "Medusa：基于多Token预测的LLM推理加速", section 3.3: sampled
+// verification draws from the tempered softmax) by inversion with the
+// caller's uniform u[b]: the first token whose cumulative probability
+// exceeds u.  One workgroup per sequence: pass 1 finds the row maximum m
+// of z = x log2(e) / temperature; pass 2 has every wave sum 2^(z - m) over
+// its own contiguous sixteenth of the row; the wave whose range holds the
+// target u * S rescans it in groups of 64 with an inclusive lane scan.
+// All sums run in a fixed order, so the draw is reproducible.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / kWave;
+constexpr int kSampleU = 8;
+
+struct SampleParams {
+    const void *logits;
+    const int32_t *rows;
+    const float *u;
+    int32_t *token;
+    int B, T, V;
+    float zscale;    // log2(e) / temperature
+};
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
+    __shared__ float red[kSampleWaves];
+    __shared__ float wsum[kSampleWaves];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int r = p.rows[b];
+    const float u = p.u[b];
+    if (r < 0 || r >= p.T || !(u >= 0.f && u < 1.f)) {
+        if (tid == 0) p.token[b] = -1;
+        return;
+    }
+    const T *row = (const T *)p.logits + ((size_t)b * p.T + r) * p.V;
+    const auto rs = make_rsrc(row, (uint32_t)p.V * (uint32_t)sizeof(T));
+    const float zs = p.zscale;
+
+    // pass 1: row maximum (in z units)
+    float mx = -INFINITY;
+    for (int v0 = tid; v0 < p.V; v0 += kSampleU * kSampleThreads) {
+        float x[kSampleU];
+#pragma unroll
+        for (int k = 0; k < kSampleU; ++k) x[k] = buf_elem<T>(rs, (uint32_t)(v0 + k * kSampleThreads));
+#pragma unroll
+        for (int k = 0; k < kSampleU; ++k)
+            if (v0 + k * kSampleThreads < p.V) mx = fmaxf(mx, x[k] * zs);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    float m = red[0];
+    for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, red[w]);
+
+    // pass 2: each wave's share of S = sum 2^(z - m)
+    const int per = (p.V + kSampleWaves - 1) / kSampleWaves;
+    const int lo = wave * per < p.V ? wave * per : p.V;
+    const int hi = lo + per < p.V ? lo + per : p.V;
+    float sum = 0.f;
+    for (int v0 = lo + lane; v0 < hi; v0 += kSampleU * kWave) {
+        float x[kSampleU];
+#pragma unroll
+        for (int k = 0; k < kSampleU; ++k) x[k] = buf_elem<T>(rs, (uint32_t)(v0 + k * kWave));
+#pragma unroll
+        for (int k = 0; k < kSampleU; ++k)
+            if (v0 + k * kWave < hi) sum += fast_exp2(x[k] * zs - m);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+    if (lane == 0) wsum[wave] = sum;
+    __syncthreads();
+
+    // the wave whose range holds the target (every thread finds the same one)
+    float S = 0.f;
+    for (int w = 0; w < kSampleWaves; ++w) S += wsum[w];
+    const float target = u * S;
+    int wsel = -1, wlast = 0;
+    float cum = 0.f, cum_last = 0.f;
+    for (int w = 0; w < kSampleWaves; ++w) {
+        if (wsum[w] > 0.f) {
+            wlast = w;
+            cum_last = cum;
+            if (wsel < 0 && cum + wsum[w] > target) {
+                wsel = w;
+                break;
+            }
+        }
+        cum += wsum[w];
+    }
+    if (wsel < 0) {   // rounding put the target past the last share: take that share
+        wsel = wlast;
+        cum = cum_last;
+    }
+    if (wave != wsel) return;
+
+    // rescan the share in groups of 64 with an inclusive lane scan
+    int tok = hi - 1;
+    float run = cum;
+    for (int base = lo; base < hi; base += kWave) {
+        const int v = base + lane;
+        const float x = buf_elem<T>(rs, (uint32_t)v);
+        float incl = v < hi ? fast_exp2(x * zs - m) : 0.f;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const float o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        const float total = __shfl(incl, kWave - 1);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(v < hi && run + incl > target);
+        if (hit != 0ull) {
+            tok = base + (int)__builtin_ctzll(hit);
+            break;
+        }
+        run += total;
+    }
+    if (lane == 0) p.token[b] = tok;
 }
 
 // host: validate the tree for acceptance (depth <= K, rank < s) and fill in
@@ -510,8 +652,9 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
     if (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16) return MEDUSA_ERR_DTYPE;
     if (B < 1 || V < 1 || K < 0 || K > MEDUSA_MAX_HEADS || s < 1 || s > 255)
         return MEDUSA_ERR_SHAPE;
-    if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL) return MEDUSA_ERR_PARAM;
-    if (mode == MEDUSA_TYPICAL &&
+    if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_TYPICAL_LOGLIK)
+        return MEDUSA_ERR_PARAM;
+    if (mode != MEDUSA_GREEDY &&
         !(temperature > 0.f && temperature < INFINITY && eps > 0.f && eps < INFINITY &&
           delta > 0.f && delta < INFINITY))
         return MEDUSA_ERR_PARAM;
@@ -537,7 +680,7 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
     p.K = K;
     p.s = s;
     p.mode = mode;
-    p.zscale = mode == MEDUSA_TYPICAL ? kLog2e / temperature : 0.f;
+    p.zscale = mode != MEDUSA_GREEDY ? kLog2e / temperature : 0.f;
     p.eps = eps;
     p.delta = delta;
     accept_chunks(B, T, V, &p.nchunk, &p.chunk);
@@ -560,6 +703,30 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
         hipLaunchKernelGGL(accept_finish_kernel<bf16_t>, dim3(B), dim3(kFinThreads), 0, sm, p);
     else
         hipLaunchKernelGGL(accept_finish_kernel<float>, dim3(B), dim3(kFinThreads), 0, sm, p);
+    return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+extern "C" int medusa_sample_token(const void *logits, const int32_t *rows, const float *u, int B,
+                                   int T, int V, int dtype, float temperature, int32_t *token,
+                                   void *stream) {
+    if (!logits || !rows || !u || !token) return MEDUSA_ERR_NULL;
+    if (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16) return MEDUSA_ERR_DTYPE;
+    if (B < 1 || T < 1 || V < 1) return MEDUSA_ERR_SHAPE;
+    if (!(temperature > 0.f && temperature < INFINITY)) return MEDUSA_ERR_PARAM;
+    SampleParams p;
+    p.logits = logits;
+    p.rows = rows;
+    p.u = u;
+    p.token = token;
+    p.B = B;
+    p.T = T;
+    p.V = V;
+    p.zscale = kLog2e / temperature;
+    hipStream_t sm = (hipStream_t)stream;
+    if (dtype == MEDUSA_BF16)
+        hipLaunchKernelGGL(sample_kernel<bf16_t>, dim3(B), dim3(kSampleThreads), 0, sm, p);
+    else
+        hipLaunchKernelGGL(sample_kernel<float>, dim3(B), dim3(kSampleThreads), 0, sm, p);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

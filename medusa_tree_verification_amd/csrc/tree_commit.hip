@@ -8,12 +8,13 @@
 // the K and V rows of the path root -> best_node[b] (in depth order) go to
 // cache positions L_b, L_b + 1, ..., and L_b advances by the path length.
 //
-// One workgroup per sequence: thread 0 reads L_b and best_node[b], walks the
-// path (parents come by value in the kernel arguments) into LDS; then every
-// thread copies 16-byte pieces of the path rows of all kv heads, with
-// kCommitU loads in flight before their stores; thread 0 finally advances
-// L_b.  Only thread 0 of the sequence's own workgroup reads or writes L_b,
-// so the update in place needs no ordering between workgroups.
+// One workgroup per sequence: the parent table (passed by value in the
+// kernel arguments) goes to LDS and thread 0 walks the path of best_node[b]
+// there; then every thread copies 16-byte pieces of the path rows of all kv
+// heads, with kCommitU loads in flight before their stores; thread 0
+// finally advances L_b.  Only the sequence's own workgroup reads or writes L_b, and its
+// write comes after a barrier that follows every read, so the update in
+// place needs no ordering between workgroups.
 #include "common.h"
 
 namespace medusa {
@@ -34,24 +35,30 @@ struct CommitParams {
 
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams p) {
     __shared__ int path[MEDUSA_MAX_TREE];
-    __shared__ int s_n, s_L;
+    __shared__ uint8_t par[MEDUSA_MAX_TREE];
+    __shared__ int s_n;
     const int b = blockIdx.x, tid = threadIdx.x;
+    // the parent table, L_b and best_node[b] are loaded together
+    if (tid < p.T) par[tid] = p.parent[tid];
+    const int L = p.prefix_len[b], best = p.best[b];
+    __syncthreads();
     if (tid == 0) {
-        const int L = p.prefix_len[b], best = p.best[b];
         int n = 0;
         if (L >= 0 && L <= p.Lcap && best >= 0 && best < p.T) {
             int depth = 0;
-            for (int a = best; p.parent[a] != 255 && depth < p.T; a = p.parent[a]) ++depth;
+            for (int a = best; par[a] != 255 && depth < p.T; a = par[a]) ++depth;
             if (L + depth + 1 <= p.Lcap) {
                 n = depth + 1;
-                for (int a = best, j = depth; j >= 0; a = p.parent[a], --j) path[j] = a;
+                for (int a = best, j = depth; j >= 0; --j) {
+                    path[j] = a;
+                    if (j > 0) a = par[a];
+                }
             }
         }
         s_n = n;
-        s_L = L;
     }
     __syncthreads();
-    const int n = s_n, L = s_L;
+    const int n = s_n;
     const int cpr = p.rowbytes / 16;                  // 16-byte pieces per row
     const int total = 2 * p.Hkv * n * cpr;
     for (int c0 = tid; c0 < total; c0 += kCommitU * kCommitThreads) {

@@ -202,14 +202,17 @@ def tree_commit_kv(k_cache, v_cache, prefix_len, k_tree, v_tree, best_node, pare
     return {"k_cache": k_cache, "v_cache": v_cache, "prefix_len": L, "committed": committed}
 
 
-def sample_token(logits, rows, u, temperature: float, dtype: str) -> Dict[str, np.ndarray]:
+def sample_token(logits, rows, u, temperature: float, dtype: str,
+                 want_cdf: bool = False) -> Dict[str, np.ndarray]:
     """The bonus token drawn from p = softmax(logits[b][rows[b]] / temperature)
     by inversion of its distribution function with the caller's uniform
     u[b] in [0, 1): the first token t whose cumulative probability
     P(<= t) exceeds u (page "Medusa：基于多Token预测的LLM推理加速", section 3.3:
     sampled verification draws from the tempered softmax).  fp64 throughout.
     Also returns, per sequence, P(< t) and P(<= t) of the drawn token; rows
-    outside [0, T) or u outside [0, 1) give token -1."""
+    outside [0, T) or u outside [0, 1) give token -1.  With want_cdf, also
+    the whole distribution function per sequence ([B][V], NaN rows where the
+    token is -1)."""
     logits = _stored(logits, dtype)
     x = logits.astype(np.float32) if dtype == "f32" else \
         (logits.astype(np.uint32) << 16).view(np.float32)
@@ -219,6 +222,7 @@ def sample_token(logits, rows, u, temperature: float, dtype: str) -> Dict[str, n
     tok = np.full(B, -1, np.int32)
     lo = np.zeros(B)
     hi = np.zeros(B)
+    cdfs = np.full((B, V), np.nan) if want_cdf else None
     for b in range(B):
         r = int(rows[b])
         if not (0 <= r < T) or not (0.0 <= u[b] < 1.0):
@@ -226,9 +230,14 @@ def sample_token(logits, rows, u, temperature: float, dtype: str) -> Dict[str, n
         z = x[b, r].astype(np.float64) / temperature
         p = np.exp(z - z.max())
         cdf = np.cumsum(p) / p.sum()
+        if want_cdf:
+            cdfs[b] = cdf
         t = int(np.searchsorted(cdf, u[b], side="right"))   # first t with cdf[t] > u
         t = min(t, V - 1)
         tok[b] = t
         lo[b] = cdf[t - 1] if t > 0 else 0.0
         hi[b] = cdf[t]
-    return {"token": tok, "cdf_lo": lo, "cdf_hi": hi}
+    out = {"token": tok, "cdf_lo": lo, "cdf_hi": hi}
+    if want_cdf:
+        out["cdf"] = cdfs
+    return out

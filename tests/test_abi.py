@@ -109,7 +109,8 @@ def test_accept_validation(mv):
                              delta, FAKE, FAKE, FAKE, None, None, ws, wsb, None)
     assert call(logits=None) == -1 and call(parent=None) == -1
     assert call(dt=3) == -3
-    assert call(mode=2) == -6
+    assert call(mode=3) == -6 and call(mode=-1) == -6
+    assert call(mode=2, temp=0.0) == -6 and call(mode=2, wsb=0) == -5
     assert call(mode=1, temp=0.0) == -6 and call(mode=1, eps=0.0) == -6
     assert call(mode=1, delta=-1.0) == -6
     assert call(mode=0, temp=0.0, wsb=0) == -5               # greedy ignores temperature
@@ -135,3 +136,15 @@ def test_commit_validation(mv):
     assert call(dt=0, dh=6) == -2 and call(T=0) == -2 and call(T=257) == -2
     assert call(parent=_i32([0, 0, 0, 1])) == -4              # root must be -1
     assert call(parent=_i32([-1, 0, 2, 1])) == -4             # parent[n] < n
+
+
+def test_sample_validation(mv):
+    L = mv.lib
+
+    def call(logits=FAKE, rows=FAKE, u=FAKE, B=2, T=4, V=100, dt=1, temp=1.0, tok=FAKE):
+        return L.medusa_sample_token(logits, rows, u, B, T, V, dt, temp, tok, None)
+    assert call(logits=None) == -1 and call(rows=None) == -1 and call(u=None) == -1
+    assert call(tok=None) == -1
+    assert call(dt=2) == -3
+    assert call(B=0) == -2 and call(T=0) == -2 and call(V=0) == -2
+    assert call(temp=0.0) == -6 and call(temp=-1.0) == -6 and call(temp=float("inf")) == -6
