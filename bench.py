@@ -144,6 +144,11 @@ def main():
            "accepted_tokens": torch.empty((B, K), **i32), "node_tokens": torch.empty((B, T), **i32),
            "next_token": torch.empty(B, **i32)}
 
+    # uniforms for the sampled bonus token (a next-row measurement)
+    uni = torch.from_numpy(np.random.default_rng(1000 * wl.cid + 13).random(B)
+                           .astype(np.float32)).to(dev)
+    samp = torch.empty(B, dtype=torch.int32, device=dev)
+
     # verification logits: planted on the candidates the heads actually propose
     mv.medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws_h)
     mv.medusa_heads_stage2(w2, B, K, d, V, s, ids, ws_h, topk_vals=vals)
@@ -230,13 +235,41 @@ def main():
         "stages": stages,
     }
 
-    result["next_rows"] = {"kv_commit": measure_commit(mv, wl, tree, kc, vc, kt, vt, plen,
-                                                       acc["best_node"], args.steps)}
+    result["next_rows"] = {
+        "kv_commit": measure_commit(mv, wl, tree, kc, vc, kt, vt, plen, acc["best_node"],
+                                    args.steps),
+        "accept_typical_loglik": time_call(
+            lambda: mv.tree_accept(vlog, ids, tree.parent, mv.TYPICAL_LOGLIK,
+                                   wl.temperature if wl.mode != "greedy" else 1.0, wl.eps,
+                                   wl.delta, ws=ws_c, out=acc), args.steps,
+            nbytes["tree_accept"]),
+        "sample_token": time_call(
+            lambda: mv.medusa_sample_token(vlog, acc["best_node"], uni,
+                                           wl.temperature if wl.mode != "greedy" else 1.0,
+                                           token=samp), args.steps,
+            B * V * (2 if wl.dtype == W.BF16 else 4)),          # the best rows, read once
+    }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, hx, ax, tree, cand, vlog_np, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
     print(json.dumps(result), flush=True)
+
+
+def time_call(fn, steps, nbytes):
+    """Mean time of one call, each bracketed by events (after 3 untimed calls)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for _ in range(3):
+        fn()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    return {"us": round(us, 2), "bytes": int(nbytes), "GBps": round(nbytes / (us * 1e-6) / 1e9, 2)}
 
 
 def measure_commit(mv, wl, tree, kc, vc, kt, vt, plen, best_node, steps):
