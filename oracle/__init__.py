@@ -241,3 +241,17 @@ def sample_token(logits, rows, u, temperature: float, dtype: str,
     if want_cdf:
         out["cdf"] = cdfs
     return out
+
+
+def lm_head_argmax(hidden, w_lm, dtype: str) -> Dict[str, np.ndarray]:
+    """Root token of the tree: the base model's own next token, the argmax
+    of its LM head W_lm h on the last hidden state h (paper explainer page,
+    section "Medusa Headのアーキテクチャ", its diagram: the original LM head
+    gives x_{t+1}, Medusa head i gives x_{t+i+1}).  fp64 over the exactly
+    decoded inputs; equal logits -> smaller id."""
+    hidden = _stored(hidden, dtype)
+    w_lm = _stored(w_lm, dtype)
+    dec = (lambda a: a.astype(np.float64)) if dtype == "f32" else \
+        (lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    logits = dec(hidden) @ dec(w_lm).T                      # [B][V]
+    return {"logits": logits, "token": np.argmax(logits, axis=1).astype(np.int32)}

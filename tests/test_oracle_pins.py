@@ -546,3 +546,35 @@ def test_sample_temperature_is_a_logit_scale():
     b = oracle.sample_token((x / np.float32(0.5)).astype(np.float32), [0, 1, 2, 0, 1], u, 1.0,
                             "f32")["token"]
     np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------- root token (next row f2)
+def test_lm_head_identity_and_planted_rows():
+    rng = np.random.default_rng(6)
+    d = 16
+    h = rng.standard_normal((3, d)).astype(np.float32)
+    # identity head: the logits are h itself
+    o = oracle.lm_head_argmax(h, np.eye(d, dtype=np.float32), "f32")
+    np.testing.assert_array_equal(o["token"], np.argmax(h, axis=1))
+    np.testing.assert_allclose(o["logits"], h.astype(np.float64), rtol=0, atol=0)
+    # a row equal to 2h dominates (Cauchy-Schwarz against rows of norm <= |h|)
+    w = rng.standard_normal((40, d)).astype(np.float32)
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    w *= np.linalg.norm(h[0]) * 0.5
+    w[29] = 2 * h[0]
+    assert oracle.lm_head_argmax(h[:1], w, "f32")["token"][0] == 29
+
+
+def test_lm_head_ties_and_bf16_decoding():
+    h = np.ones((1, 8), np.float32)
+    w = np.zeros((6, 8), np.float32)
+    w[2] = w[4] = 1.0 / 8                 # equal logits 1.0 at ids 2 and 4
+    assert oracle.lm_head_argmax(h, w, "f32")["token"][0] == 2
+    # bf16 bit patterns decode exactly: same as their fp32 values
+    rng = np.random.default_rng(7)
+    hb = W.encode(rng.standard_normal((2, 32)), W.BF16)
+    wb = W.encode(rng.standard_normal((50, 32)), W.BF16)
+    a = oracle.lm_head_argmax(hb, wb, "bf16")
+    b = oracle.lm_head_argmax(W.decode(hb, W.BF16).astype(np.float32),
+                              W.decode(wb, W.BF16).astype(np.float32), "f32")
+    np.testing.assert_array_equal(a["token"], b["token"])
