@@ -144,6 +144,12 @@ def main():
            "accepted_tokens": torch.empty((B, K), **i32), "node_tokens": torch.empty((B, T), **i32),
            "next_token": torch.empty(B, **i32)}
 
+    # LM-head weights for the root-token variant of the heads (a next-row
+    # measurement): random, N(0, 0.02), in the workload's dtype
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * wl.cid + 14)
+    w_lm = (torch.randn((V, d), generator=gen, device=dev) * 0.02).to(w2.dtype)
+
     # uniforms for the sampled bonus token (a next-row measurement)
     uni = torch.from_numpy(np.random.default_rng(1000 * wl.cid + 13).random(B)
                            .astype(np.float32)).to(dev)
@@ -243,6 +249,9 @@ def main():
                                    wl.temperature if wl.mode != "greedy" else 1.0, wl.eps,
                                    wl.delta, ws=ws_c, out=acc), args.steps,
             nbytes["tree_accept"]),
+        "heads_with_root": time_call(
+            lambda: mv.medusa_heads_topk_root(hidden, w1, w2, w_lm, s, ws=ws_h), args.steps,
+            nbytes["heads_stage1"] + nbytes["heads_stage2"] + V * d * w_lm.element_size()),
         "sample_token": time_call(
             lambda: mv.medusa_sample_token(vlog, acc["best_node"], uni,
                                            wl.temperature if wl.mode != "greedy" else 1.0,

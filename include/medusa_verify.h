@@ -111,6 +111,24 @@ int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, int s, int d
 
 size_t medusa_heads_topk_workspace_bytes(int B, int K, int d, int V, int s, int dtype);
 
+/* medusa_heads_topk plus the tree's root token: the base model's own next
+ * token, the argmax of its LM head w_lm on the same hidden state (paper
+ * explainer page, section "Medusa Headのアーキテクチャ", its diagram: the
+ * original LM head gives x_{t+1}, Medusa head i gives x_{t+i+1}).  The LM
+ * head's weights ride along in stage 2's weight stream as one more head
+ * (input: the hidden state itself, no SiLU block).
+ *
+ *   w_lm        device [V][d] dtype ([out][in])
+ *   root_token  device [B] int32: argmax_v (w_lm h)_v, equal logits ->
+ *               smaller id
+ *   root_val    device [B] float32 logit of root_token, or NULL
+ * Other arguments, limits and the workspace as medusa_heads_topk
+ * (logits_out covers the K Medusa heads only). */
+int medusa_heads_topk_root(const void *hidden, const void *w1, const void *w2, const void *w_lm,
+                           int B, int K, int d, int V, int s, int dtype, float *logits_out,
+                           int32_t *topk_ids, float *topk_vals, int32_t *root_token,
+                           float *root_val, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * tree_attention -- one attention pass over the candidate tree.
  *

@@ -25,7 +25,8 @@ STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "ME
           -4: "MEDUSA_ERR_TREE", -5: "MEDUSA_ERR_WORKSPACE", -6: "MEDUSA_ERR_PARAM",
           -7: "MEDUSA_ERR_LAUNCH"}
 
-EXPORTS = ["medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2",
+EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
+           "medusa_heads_stage2",
            "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
            "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
            "medusa_status_str",
@@ -45,6 +46,7 @@ def _load() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.medusa_heads_topk.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    L.medusa_heads_topk_root.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, Z, P]
     L.medusa_heads_stage1.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
     L.medusa_heads_stage2.argtypes = [P, I, I, I, I, I, I, P, P, P, P, Z, P]
     L.medusa_heads_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -60,7 +62,8 @@ def _load() -> ctypes.CDLL:
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
-    for f in ("medusa_heads_topk", "medusa_heads_stage1", "medusa_heads_stage2", "tree_attention",
+    for f in ("medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
+              "medusa_heads_stage2", "tree_attention",
               "tree_accept", "tree_commit_kv", "medusa_sample_token"):
         getattr(L, f).restype = I
     return L
@@ -237,3 +240,28 @@ def medusa_sample_token(logits: torch.Tensor, rows: torch.Tensor, u: torch.Tenso
                                  float(temperature), _ptr(token), _stream(stream))
     _check("medusa_sample_token", rc)
     return token
+
+
+def medusa_heads_topk_root(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+                           w_lm: torch.Tensor, s: int, *, ws: Optional[torch.Tensor] = None,
+                           stream=None) -> Dict[str, torch.Tensor]:
+    """The K heads' top-s plus the root token (argmax of the LM head w_lm on
+    the hidden state), in one weight stream."""
+    for t, n in ((hidden, "hidden"), (w1, "w1"), (w2, "w2"), (w_lm, "w_lm")):
+        _need(t, n)
+    B, d = hidden.shape
+    K, V = w2.shape[0], w2.shape[1]
+    dt = _dtype_code(hidden)
+    dev = hidden.device
+    out = {"topk_ids": torch.empty((B, K, s), dtype=torch.int32, device=dev),
+           "topk_vals": torch.empty((B, K, s), dtype=torch.float32, device=dev),
+           "root_token": torch.empty(B, dtype=torch.int32, device=dev),
+           "root_val": torch.empty(B, dtype=torch.float32, device=dev)}
+    if ws is None:
+        ws = workspace(lib.medusa_heads_topk_workspace_bytes(B, K, d, V, s, dt), dev)
+    rc = lib.medusa_heads_topk_root(_ptr(hidden), _ptr(w1), _ptr(w2), _ptr(w_lm), B, K, d, V, s,
+                                    dt, None, _ptr(out["topk_ids"]), _ptr(out["topk_vals"]),
+                                    _ptr(out["root_token"]), _ptr(out["root_val"]), _ptr(ws),
+                                    ws.numel(), _stream(stream))
+    _check("medusa_heads_topk_root", rc)
+    return out

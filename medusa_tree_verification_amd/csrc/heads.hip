@@ -54,19 +54,20 @@ constexpr int kS2MaxWG = MEDUSA_S2_WG_PER_CU * kNumCU;   // stage 2: workgroups
 
 struct HeadsLayout {
     size_t z_off, part_off, total;
-    int ntph, nt, P;
+    int nh, ntph, nt, P;   // nh: streamed heads (K, plus the LM head when it rides along)
 };
 
 inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
 
-inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype) {
+inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype, int lm = 1) {
     HeadsLayout L;
+    L.nh = K + (lm ? 1 : 0);
     L.ntph = (V + 15) / 16;
-    L.nt = K * L.ntph;
+    L.nt = L.nh * L.ntph;
     L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
     L.z_off = 0;
     L.part_off = align_up((size_t)B * K * d * esize(dtype), 256);
-    L.total = L.part_off + align_up((size_t)K * B * L.P * kSMax * 2 * sizeof(float), 256);
+    L.total = L.part_off + align_up((size_t)L.nh * B * L.P * kSMax * 2 * sizeof(float), 256);
     return L;
 }
 
@@ -275,7 +276,9 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
 // wave + kS2Waves, ...
 __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part,
                                                  int32_t *__restrict__ topk_ids,
-                                                 float *__restrict__ topk_vals, int head, int B,
+                                                 float *__restrict__ topk_vals,
+                                                 int32_t *__restrict__ root_token,
+                                                 float *__restrict__ root_val, int head, int B,
                                                  int K, int s, int ntph, int nt, int P, int wave,
                                                  int lane) {
     const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
@@ -298,11 +301,16 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
         int oi[kSMax];
         group_merge(M, s, 1, ov, oi);
         if (lane == 0) {
+            if (head == K) {   // the LM head: its argmax is the root token
+                root_token[col] = oi[0];
+                if (root_val) root_val[col] = ov[0];
+            } else {
 #pragma unroll
-            for (int r = 0; r < kSMax; ++r) {
-                if (r >= s) continue;
-                topk_ids[((size_t)col * K + head) * s + r] = oi[r];
-                if (topk_vals) topk_vals[((size_t)col * K + head) * s + r] = ov[r];
+                for (int r = 0; r < kSMax; ++r) {
+                    if (r >= s) continue;
+                    topk_ids[((size_t)col * K + head) * s + r] = oi[r];
+                    if (topk_vals) topk_vals[((size_t)col * K + head) * s + r] = ov[r];
+                }
             }
         }
     }
@@ -310,8 +318,9 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
 
 template <typename T>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
-    const T *__restrict__ w2, const T *__restrict__ z, float *__restrict__ logits_out,
-    float2 *__restrict__ part, int B, int K, int d, int V, int s, int ntph, int nt, int P) {
+    const T *__restrict__ w2, const T *__restrict__ z, const T *__restrict__ w_lm,
+    const T *__restrict__ hidden, float *__restrict__ logits_out, float2 *__restrict__ part, int B,
+    int K, int d, int V, int s, int ntph, int nt, int P) {
     constexpr int KC = Elem<T>::kPer16B;
     // per-wave merged lists: [wave][head slot 0/1][column][s]
     __shared__ float2 stage[kS2Waves][2][16][kSMax];
@@ -364,8 +373,11 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
         f32x4 acc[kS2Tiles];
 #pragma unroll
         for (int r = 0; r < kS2Tiles; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T *brow = z + ((size_t)(bcol ? c : B - 1) * K + head) * d + g * KC;
-        const T *wbase = w2 + (size_t)head * V * d + g * KC;
+        // head K (when streamed) is the LM head: weights w_lm, input the hidden state
+        const int bc = bcol ? c : B - 1;
+        const T *brow = head < K ? z + ((size_t)bc * K + head) * d + g * KC
+                                 : hidden + (size_t)bc * d + g * KC;
+        const T *wbase = head < K ? w2 + (size_t)head * V * d + g * KC : w_lm + g * KC;
         // n is wave-uniform: one straight-line body per tile count
         switch (n) {
             case 1: stream_tiles<T, 1>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
             if (r >= n) continue;
             const int v0 = (tile_in_head + r) * 16 + 4 * g;
             if (bcol) {
-                if (logits_out) {
+                if (logits_out && head < K) {
                     float *dst = logits_out + ((size_t)c * K + head) * V + v0;
                     if (v0 + 3 < V && ((V & 3) == 0)) {
                         *reinterpret_cast<f32x4 *>(dst) = acc[r];
@@ -447,9 +459,10 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
 // workgroups that own its tiles, merged with one wave per column.
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_merge_kernel(
     const float2 *__restrict__ part, int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals,
-    int B, int K, int s, int ntph, int nt, int P) {
-    merge_head_lists(part, topk_ids, topk_vals, (int)blockIdx.x, B, K, s, ntph, nt, P,
-                     (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
+    int32_t *__restrict__ root_token, float *__restrict__ root_val, int B, int K, int s, int ntph,
+    int nt, int P) {
+    merge_head_lists(part, topk_ids, topk_vals, root_token, root_val, (int)blockIdx.x, B, K, s,
+                     ntph, nt, P, (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
 }
 
 // --------------------------------------------------------------- host side
@@ -484,23 +497,29 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
-int launch_stage2(const void *w2, int B, int K, int d, int V, int s, int dtype, float *logits_out,
-                  int32_t *topk_ids, float *topk_vals, void *ws, hipStream_t st) {
-    const HeadsLayout L = heads_layout(B, K, d, V, dtype);
+// w_lm == NULL: the K Medusa heads only; otherwise the LM head (input: the
+// hidden state) is streamed as head K and its argmax goes to root_token.
+int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, int K, int d,
+                  int V, int s, int dtype, float *logits_out, int32_t *topk_ids,
+                  float *topk_vals, int32_t *root_token, float *root_val, void *ws,
+                  hipStream_t st) {
+    const HeadsLayout L = heads_layout(B, K, d, V, dtype, w_lm != nullptr);
     char *base = (char *)ws;
     float2 *part = (float2 *)(base + L.part_off);
     const dim3 grid((unsigned)L.P), block(kS2Waves * kWave);
     if (dtype == MEDUSA_BF16)
         hipLaunchKernelGGL(heads_stage2_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)w2,
-                           (const bf16_t *)(base + L.z_off), logits_out, part, B, K, d, V, s,
-                           L.ntph, L.nt, L.P);
+                           (const bf16_t *)(base + L.z_off), (const bf16_t *)w_lm,
+                           (const bf16_t *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
+                           L.P);
     else
         hipLaunchKernelGGL(heads_stage2_kernel<float>, grid, block, 0, st, (const float *)w2,
-                           (const float *)(base + L.z_off), logits_out, part, B, K, d, V, s,
-                           L.ntph, L.nt, L.P);
+                           (const float *)(base + L.z_off), (const float *)w_lm,
+                           (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
+                           L.P);
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
-    hipLaunchKernelGGL(heads_merge_kernel, dim3((unsigned)K), block, 0, st, part, topk_ids,
-                       topk_vals, B, K, s, L.ntph, L.nt, L.P);
+    hipLaunchKernelGGL(heads_merge_kernel, dim3((unsigned)L.nh), block, 0, st, part, topk_ids,
+                       topk_vals, root_token, root_val, B, K, s, L.ntph, L.nt, L.P);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
@@ -532,8 +551,8 @@ extern "C" int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, i
     if (!topk_ids) return MEDUSA_ERR_NULL;
     st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
     if (st != MEDUSA_OK) return st;
-    return launch_stage2(w2, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals, ws,
-                         (hipStream_t)stream);
+    return launch_stage2(w2, nullptr, nullptr, B, K, d, V, s, dtype, logits_out, topk_ids,
+                         topk_vals, nullptr, nullptr, ws, (hipStream_t)stream);
 }
 
 extern "C" int medusa_heads_topk(const void *hidden, const void *w1, const void *w2, int B, int K,
@@ -547,6 +566,22 @@ extern "C" int medusa_heads_topk(const void *hidden, const void *w1, const void 
     if (st != MEDUSA_OK) return st;
     st = launch_stage1(hidden, w1, B, K, d, V, dtype, ws, (hipStream_t)stream);
     if (st != MEDUSA_OK) return st;
-    return launch_stage2(w2, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals, ws,
-                         (hipStream_t)stream);
+    return launch_stage2(w2, nullptr, nullptr, B, K, d, V, s, dtype, logits_out, topk_ids,
+                         topk_vals, nullptr, nullptr, ws, (hipStream_t)stream);
+}
+
+extern "C" int medusa_heads_topk_root(const void *hidden, const void *w1, const void *w2,
+                                      const void *w_lm, int B, int K, int d, int V, int s,
+                                      int dtype, float *logits_out, int32_t *topk_ids,
+                                      float *topk_vals, int32_t *root_token, float *root_val,
+                                      void *ws, size_t ws_bytes, void *stream) {
+    int st = check_heads_args(w2, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!hidden || !w1 || !w_lm || !topk_ids || !root_token) return MEDUSA_ERR_NULL;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    st = launch_stage1(hidden, w1, B, K, d, V, dtype, ws, (hipStream_t)stream);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2(w2, w_lm, hidden, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals,
+                         root_token, root_val, ws, (hipStream_t)stream);
 }

@@ -95,3 +95,64 @@ def test_heads_stages_equal_fused_call_and_repeat_bit_identical():
         assert torch.equal(ids, a["topk_ids"]) and torch.equal(vals, a["topk_vals"])
         assert torch.equal(lg, a["logits"])
     del wl
+
+
+# ---------------------------------------------------------------- root token
+def _root_run(hx, s):
+    from medusa_tree_verification_amd import binding as mv
+    out = mv.medusa_heads_topk_root(to_dev(hx["hidden"]), to_dev(hx["w1"]), to_dev(hx["w2"]),
+                                    to_dev(hx["w_lm"]), s)
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _root_check(out, hx, dtype):
+    """The GPU's root must be the oracle's argmax unless the oracle's top two
+    logits are within the GPU's own logit error (then it must be within that
+    error of the maximum).  Returns the number of such near-tie rows."""
+    ref = oracle.lm_head_argmax(hx["hidden"], hx["w_lm"], dtype)
+    lg = ref["logits"]
+    near = 0
+    for b in range(lg.shape[0]):
+        t = int(out["root_token"][b])
+        band = 4 * max(abs(float(out["root_val"][b]) - lg[b, t]), 1e-6 * np.abs(lg[b]).max())
+        top2 = np.sort(lg[b])[-2:] if lg.shape[1] > 1 else np.array([lg[b, 0], -np.inf])
+        assert lg[b, t] >= top2[-1] - band, (b, t, lg[b, t], top2)
+        if top2[-1] - top2[-2] > band:
+            assert t == ref["token"][b]
+        else:
+            near += 1
+    return near
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,K,d,V,s", [(1, 1, 128, 16, 1), (3, 2, 384, 777, 8),
+                                       (16, 5, 256, 4099, 3), (7, 4, 128, 70000, 3)])
+def test_heads_root_random(dtype, B, K, d, V, s):
+    seed = hash((B, K, d, V, s, 7)) % 10000 * 10
+    hx = _random_heads(seed, B, K, d, V, dtype)
+    hx["w_lm"] = W.normal_tensor(seed + 4, (V, d), 0.05, dtype)
+    out = _root_run(hx, s)
+    # the Medusa heads' results are those of the plain call (the extra head
+    # moves the work split, hence the order of the k-sums: values agree to
+    # rounding, ids except where two candidates are that close)
+    plain = _run(hx, s, dtype)
+    np.testing.assert_allclose(out["topk_vals"], plain["topk_vals"], rtol=1e-5, atol=1e-6)
+    diff = out["topk_ids"] != plain["topk_ids"]
+    np.testing.assert_allclose(out["topk_vals"][diff], plain["topk_vals"][diff], rtol=1e-5)
+    assert _root_check(out, hx, dtype) <= max(1, B // 8)
+
+
+def test_heads_root_workload_shape():
+    """Llama-7B shapes (d 4096, V 32000, bf16) with a planted root per row."""
+    wl = W.WORKLOADS["ragged_b16_gqa_typical"]
+    hx = W.heads_inputs(wl)
+    w_lm = W.normal_tensor(1000 * wl.cid + 20, (wl.V, wl.d), 0.02, wl.dtype)
+    h = W.decode(hx["hidden"], wl.dtype)
+    rng = np.random.default_rng(21)
+    plant = rng.choice(wl.V, wl.B, replace=False)
+    for b in range(wl.B):
+        w_lm[plant[b]] = W.encode(h[b] / np.linalg.norm(h[b]) * 0.5, wl.dtype)
+    hx["w_lm"] = w_lm
+    out = _root_run(hx, wl.s)
+    assert _root_check(out, hx, wl.dtype) == 0
+    np.testing.assert_array_equal(out["root_token"], plant)
