@@ -316,7 +316,9 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
     }
 }
 
-template <typename T>
+// LM: the LM head rides along as head K (a separate instantiation, so the
+// plain and the root-token streams show up as different kernels in traces).
+template <typename T, bool LM>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, const T *__restrict__ w_lm,
     const T *__restrict__ hidden, float *__restrict__ logits_out, float2 *__restrict__ part, int B,
@@ -375,9 +377,10 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
         for (int r = 0; r < kS2Tiles; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         // head K (when streamed) is the LM head: weights w_lm, input the hidden state
         const int bc = bcol ? c : B - 1;
-        const T *brow = head < K ? z + ((size_t)bc * K + head) * d + g * KC
-                                 : hidden + (size_t)bc * d + g * KC;
-        const T *wbase = head < K ? w2 + (size_t)head * V * d + g * KC : w_lm + g * KC;
+        const bool lmh = LM && head == K;
+        const T *brow = lmh ? hidden + (size_t)bc * d + g * KC
+                            : z + ((size_t)bc * K + head) * d + g * KC;
+        const T *wbase = lmh ? w_lm + g * KC : w2 + (size_t)head * V * d + g * KC;
         // n is wave-uniform: one straight-line body per tile count
         switch (n) {
             case 1: stream_tiles<T, 1>(acc, wbase, brow, tile_in_head, V, d, c, rot); break;
@@ -507,16 +510,20 @@ int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, i
     char *base = (char *)ws;
     float2 *part = (float2 *)(base + L.part_off);
     const dim3 grid((unsigned)L.P), block(kS2Waves * kWave);
-    if (dtype == MEDUSA_BF16)
-        hipLaunchKernelGGL(heads_stage2_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)w2,
+    const bool lm = w_lm != nullptr;
+    if (dtype == MEDUSA_BF16) {
+        auto *kern = lm ? heads_stage2_kernel<bf16_t, true> : heads_stage2_kernel<bf16_t, false>;
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)w2,
                            (const bf16_t *)(base + L.z_off), (const bf16_t *)w_lm,
                            (const bf16_t *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
                            L.P);
-    else
-        hipLaunchKernelGGL(heads_stage2_kernel<float>, grid, block, 0, st, (const float *)w2,
+    } else {
+        auto *kern = lm ? heads_stage2_kernel<float, true> : heads_stage2_kernel<float, false>;
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)w2,
                            (const float *)(base + L.z_off), (const float *)w_lm,
                            (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
                            L.P);
+    }
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     hipLaunchKernelGGL(heads_merge_kernel, dim3((unsigned)L.nh), block, 0, st, part, topk_ids,
                        topk_vals, root_token, root_val, B, K, s, L.ntph, L.nt, L.P);
