@@ -235,7 +235,7 @@ def main():
                                                      int(ax["prefix_len"].max())],
                    "acceptance": wl.mode, "parallelism": "single GPU"},
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"kernel": "heads_stage2_kernel (W2 stream + top-s)", "bound": "hbm",
+        "roofline": {"kernel": "medusa_heads_stage2: heads_stage2_kernel + heads_merge_kernel (W2 stream + top-s)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "stages": stages,
