@@ -272,8 +272,8 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
 }
 
 // Merge the partial top-s lists of head `head` (one per workgroup owning a
-// tile of it) into topk_ids / topk_vals: wave `wave` takes columns wave,
-// wave + kS2Waves, ...
+// tile of it) into topk_ids / topk_vals: wave `wave` of workgroup row
+// blockIdx.y takes column blockIdx.y * kS2Waves + wave.
 __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part,
                                                  int32_t *__restrict__ topk_ids,
                                                  float *__restrict__ topk_vals,
@@ -285,18 +285,24 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
     const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
     const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
     const int nparts = wg_last - wg_first + 1;
-    for (int col = wave; col < B; col += kS2Waves) {
+    const int col = (int)blockIdx.y * kS2Waves + wave;   // one wave per (head, column)
+    if (col < B) {
         TopList M;
         M.clear();
         const float2 *src = part + ((size_t)head * B + col) * P * kSMax;
-        for (int p = lane; p < nparts; p += kWave)
+        for (int p0 = 0; p0 < nparts; p0 += kWave) {
+            // the lane's s entries are loaded before any is inserted
+            const int p = p0 + lane;
+            const float2 *lp = src + (size_t)(p < nparts ? p : nparts - 1) * kSMax;
+            float2 e[kSMax];
+#pragma unroll
+            for (int r = 0; r < kSMax; ++r) e[r] = r < s ? lp[r] : make_float2(0.f, 0.f);
 #pragma unroll
             for (int r = 0; r < kSMax; ++r) {
-                if (r >= s) continue;
-                const float2 e = src[(size_t)p * kSMax + r];
-                const int id = __float_as_int(e.y);
-                if (id != 0x7FFFFFFF) M.insert(e.x, id, s);
+                const int id = (p < nparts && r < s) ? __float_as_int(e[r].y) : 0x7FFFFFFF;
+                if (id != 0x7FFFFFFF) M.insert(e[r].x, id, s);
             }
+        }
         float ov[kSMax];
         int oi[kSMax];
         group_merge(M, s, 1, ov, oi);
@@ -525,7 +531,9 @@ int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, i
                            L.P);
     }
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
-    hipLaunchKernelGGL(heads_merge_kernel, dim3((unsigned)L.nh), block, 0, st, part, topk_ids,
+    hipLaunchKernelGGL(heads_merge_kernel,
+                       dim3((unsigned)L.nh, (unsigned)((B + kS2Waves - 1) / kS2Waves)), block, 0,
+                       st, part, topk_ids,
                        topk_vals, root_token, root_val, B, K, s, L.ntph, L.nt, L.P);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }

@@ -366,15 +366,19 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
     // stages before it is written to LDS, so PD stages of bytes are in flight
     constexpr int PD = sizeof(T) == 2 ? kPD : 1;   // fp32 stages are twice as large
     StageCopy<T, DH, NT> cp[PD];
+    // Stages past the last are issued as empty ranges (their loads return
+    // zeros without touching memory), so that every load and store below is
+    // unconditional: the compiler then knows exactly how many loads are
+    // younger than the ones a store waits for, and keeps PD stages in flight.
     auto issue = [&](StageCopy<T, DH, NT> &dst, int sidx) __attribute__((always_inline)) {
-        const T *kb, *vb;
-        int nv;
+        const T *kb = kcb, *vb = vcb;
+        int nv = 0;
         if (sidx < npre) {
             const int k0 = kbeg + sidx * kBN;
             nv = kend - k0 < kBN ? kend - k0 : kBN;
             kb = kcb + (size_t)k0 * DH;
             vb = vcb + (size_t)k0 * DH;
-        } else {
+        } else if (sidx < nstage) {
             const int tb = (sidx - npre) * kBN;
             nv = ntree - tb < kBN ? ntree - tb : kBN;
             kb = ktb + (size_t)tb * DH;
@@ -387,20 +391,20 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
     // buffer i%2, then stage i+1 (loads issued PD stages earlier) is written
     // to the other buffer and the loads of stage i+1+PD go out into the
     // register set it freed.  The loop is unrolled by PD so that every
-    // register set is named statically.
+    // register set is named statically; it runs a multiple of PD stages, the
+    // ones past the last computing nothing.
     // prologue: stages 0 .. PD-1 in flight, stage 0 to LDS, stage PD issued
 #pragma unroll
-    for (int k = 0; k < PD; ++k)
-        if (k < nstage) issue(cp[k], k);
+    for (int k = 0; k < PD; ++k) issue(cp[k], k);
     cp[0].store(lds[0], tid);
-    if (PD < nstage) issue(cp[0], PD);
+    issue(cp[0], PD);
     __syncthreads();
-    for (int base = 0; base < nstage; base += PD) {
+    const int nstage_pad = (nstage + PD - 1) / PD * PD;
+    for (int base = 0; base < nstage_pad; base += PD) {
 #pragma unroll
         for (int k = 0; k < PD; ++k) {   // unrolled: register set (k + 1) % PD is static
             const int sidx = base + k;
-            if (sidx >= nstage) break;
-            if (computes) {
+            if (computes && sidx < nstage) {
                 int kind = 0, klim = kBN;
                 uint64_t mword = 0ull;
                 if (sidx < npre) {
@@ -415,10 +419,8 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
                 attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword,
                                     cscale, sub_lo, sub_hi);
             }
-            if (sidx + 1 < nstage) {
-                cp[(k + 1) % PD].store(lds[(sidx + 1) & 1], tid);
-                if (sidx + 1 + PD < nstage) issue(cp[(k + 1) % PD], sidx + 1 + PD);
-            }
+            cp[(k + 1) % PD].store(lds[(sidx + 1) & 1], tid);
+            issue(cp[(k + 1) % PD], sidx + 1 + PD);
             __syncthreads();
         }
     }
