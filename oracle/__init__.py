@@ -255,3 +255,94 @@ def lm_head_argmax(hidden, w_lm, dtype: str) -> Dict[str, np.ndarray]:
         (lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
     logits = dec(hidden) @ dec(w_lm).T                      # [B][V]
     return {"logits": logits, "token": np.argmax(logits, axis=1).astype(np.int32)}
+
+
+# ------------------------------------------------------------------
+# Multi-layer synthetic verify forward (a second workload for the tree pass)
+# ------------------------------------------------------------------
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 -> the stored dtype and back: fp32 rounding, then (bf16) the
+    upper 16 bits rounded to nearest-even."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored bits (bf16) or fp32 values -> fp64."""
+    a = _stored(a, dtype)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 values already representable in dtype -> stored form."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    return f if dtype == "f32" else (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary position embedding on the last axis (dh), pairs (j, j + dh/2):
+    angle pos * theta^(-2j/dh).  x: [..., n, dh] with pos broadcast to [..., n]."""
+    dh = x.shape[-1]
+    half = dh // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / dh)
+    ang = np.asarray(pos, np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def verify_forward(h0, layers, g_final, w_lm, k_caches, v_caches, prefix_len, parent,
+                   Hq: int, Hkv: int, dh: int, dtype: str, theta: float = 10000.0,
+                   eps: float = 1e-6) -> Dict[str, np.ndarray]:
+    """N attention blocks over the tree tokens, then the LM head.
+
+    The tree pass is one forward pass over all candidates with the tree mask
+    (paper explainer page, tree-attention section); page
+    "Medusa：基于多Token预测的LLM推理加速", section 5.3, runs the model once over
+    the flattened tree and reads the logits of every position.  Each block:
+    x = rmsnorm(h) g (rounded to dtype); q, k, v = x W^T (rounded after the
+    rotary embedding of q and k at position L_b + depth(n)); o = tree
+    attention over the block's cached prefix and the node's ancestors-or-self
+    (rounded); h += o Wo^T (fp64 residual stream).  Finally
+    logits = (rmsnorm(h) g_final, rounded) W_lm^T.  layers: a list of dicts
+    with g, wq, wk, wv, wo in stored form; caches [B][Hkv][Lcap][dh] hold
+    post-rotary keys.  Returns logits [B][T][V] and each block's tree k, v in
+    stored form ([N][B][Hkv][T][dh])."""
+    h = decode(h0, dtype)                         # [B][T][d]
+    B, T, d = h.shape
+    parent = _c(parent, np.int32)
+    prefix_len = _c(prefix_len, np.int32)
+    depth = tree(parent, T, max(T, 1))["depth"]
+    Lcap = np.asarray(k_caches[0]).shape[2]
+    pos = np.minimum(np.maximum(prefix_len, 0), Lcap)[:, None] + depth[None, :]   # [B][T]
+    ks, vs = [], []
+    for lw in layers:
+        x = round_to(rmsnorm(h, decode(lw["g"], dtype), eps), dtype)
+        q = (x @ decode(lw["wq"], dtype).T).reshape(B, T, Hq, dh).transpose(0, 2, 1, 3)
+        k = (x @ decode(lw["wk"], dtype).T).reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)
+        v = (x @ decode(lw["wv"], dtype).T).reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)
+        q = round_to(rope(q, pos[:, None, :], theta), dtype)
+        k = round_to(rope(k, pos[:, None, :], theta), dtype)
+        v = round_to(v, dtype)
+        kq, kk, kv = encode(q, dtype), encode(k, dtype), encode(v, dtype)
+        ks.append(kk)
+        vs.append(kv)
+        o = tree_attention(kq, k_caches[len(ks) - 1], v_caches[len(vs) - 1], prefix_len, kk, kv,
+                           parent, 1.0 / np.sqrt(dh), dtype)
+        o = round_to(o, dtype).transpose(0, 2, 1, 3).reshape(B, T, Hq * dh)
+        h = h + o @ decode(lw["wo"], dtype).T
+    x = round_to(rmsnorm(h, decode(g_final, dtype), eps), dtype)
+    logits = x @ decode(w_lm, dtype).T
+    return {"logits": logits, "hidden": h, "k_tree": np.stack(ks) if ks else None,
+            "v_tree": np.stack(vs) if vs else None}

@@ -578,3 +578,121 @@ def test_lm_head_ties_and_bf16_decoding():
     b = oracle.lm_head_argmax(W.decode(hb, W.BF16).astype(np.float32),
                               W.decode(wb, W.BF16).astype(np.float32), "f32")
     np.testing.assert_array_equal(a["token"], b["token"])
+
+
+# ------------------------------------------------------- multi-layer verify forward (next row f4)
+def test_round_to_bf16_matches_torch():
+    import torch
+    x = np.random.default_rng(1).standard_normal(1000) * 10
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to(x, "bf16"), ref)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((5, 64))
+    k = rng.standard_normal((5, 64))
+    np.testing.assert_allclose(oracle.rope(q, np.zeros(5), 1e4), q, atol=1e-15)
+    # each (j, j + dh/2) pair keeps its norm
+    r = oracle.rope(q, np.arange(5) * 37.0, 1e4)
+    np.testing.assert_allclose(r[:, :32] ** 2 + r[:, 32:] ** 2, q[:, :32] ** 2 + q[:, 32:] ** 2,
+                               rtol=1e-12)
+    # the score depends on the position difference only
+    m, n = np.array([40.0, 7.0, 1000.0, 3.0, 0.0]), np.array([3.0, 7.0, 999.0, 30.0, 5.0])
+    a = np.sum(oracle.rope(q, m, 1e4) * oracle.rope(k, n, 1e4), axis=1)
+    b = np.sum(oracle.rope(q, m - n, 1e4) * k, axis=1)
+    np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def test_rmsnorm_unit_rms():
+    x = np.random.default_rng(3).standard_normal((4, 256)) * 5
+    y = oracle.rmsnorm(x, np.ones(256), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12)
+
+
+def _fwd_inputs(seed, B, T, d, Hq, Hkv, dh, V, Lcap, N, dtype):
+    rng = np.random.default_rng(seed)
+    enc = lambda a: oracle.encode(oracle.round_to(a, dtype), dtype)
+    layers = [{"g": enc(1 + 0.1 * rng.standard_normal(d)),
+               "wq": enc(rng.standard_normal((Hq * dh, d)) / np.sqrt(d)),
+               "wk": enc(rng.standard_normal((Hkv * dh, d)) / np.sqrt(d)),
+               "wv": enc(rng.standard_normal((Hkv * dh, d)) / np.sqrt(d)),
+               "wo": enc(rng.standard_normal((d, Hq * dh)) / np.sqrt(Hq * dh))} for _ in range(N)]
+    kc = [enc(rng.standard_normal((B, Hkv, Lcap, dh))) for _ in range(N)]
+    vc = [enc(rng.standard_normal((B, Hkv, Lcap, dh))) for _ in range(N)]
+    return dict(h0=enc(rng.standard_normal((B, T, d))), layers=layers,
+                g_final=enc(np.ones(d)), w_lm=enc(rng.standard_normal((V, d)) / np.sqrt(d)),
+                k_caches=kc, v_caches=vc)
+
+
+def _causal_forward(x, Lb, layers, g_final, w_lm, kc, vc, Hq, Hkv, dh, dtype, b):
+    """Plain causal decoding of one sequence: token i at position Lb + i sees
+    the cached prefix and tokens 0..i (torch's scaled_dot_product_attention
+    with is_causal-style masking)."""
+    import torch
+    dec = lambda a: oracle.decode(a, dtype)
+    h = dec(x)                                       # [n][d]
+    n = h.shape[0]
+    pos = Lb + np.arange(n, dtype=np.float64)
+    G = Hq // Hkv
+    for li, lw in enumerate(layers):
+        xn = oracle.round_to(oracle.rmsnorm(h, dec(lw["g"]), 1e-6), dtype)
+        q = oracle.round_to(oracle.rope((xn @ dec(lw["wq"]).T).reshape(n, Hq, dh).transpose(1, 0, 2),
+                                        pos, 1e4), dtype)
+        k = oracle.round_to(oracle.rope((xn @ dec(lw["wk"]).T).reshape(n, Hkv, dh).transpose(1, 0, 2),
+                                        pos, 1e4), dtype)
+        v = oracle.round_to((xn @ dec(lw["wv"]).T).reshape(n, Hkv, dh).transpose(1, 0, 2), dtype)
+        K = np.concatenate([dec(kc[li])[b, :, :Lb], k], axis=1)
+        Vv = np.concatenate([dec(vc[li])[b, :, :Lb], v], axis=1)
+        mask = np.concatenate([np.ones((n, Lb), bool), np.tril(np.ones((n, n), bool))], axis=1)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(np.repeat(K, G, axis=0)),
+            torch.from_numpy(np.repeat(Vv, G, axis=0)), attn_mask=torch.from_numpy(mask)).numpy()
+        o = oracle.round_to(o, dtype).transpose(1, 0, 2).reshape(n, Hq * dh)
+        h = h + o @ dec(lw["wo"]).T
+    xf = oracle.round_to(oracle.rmsnorm(h, dec(g_final), 1e-6), dtype)
+    return xf @ dec(w_lm).T
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_chain_tree_is_causal_decoding(dtype):
+    B, T, d, Hq, Hkv, dh, V, Lcap, N = 2, 6, 64, 4, 2, 16, 50, 12, 2
+    I = _fwd_inputs(11, B, T, d, Hq, Hkv, dh, V, Lcap, N, dtype)
+    parent = np.arange(-1, T - 1, dtype=np.int32)
+    L = np.array([12, 5], np.int32)
+    o = oracle.verify_forward(I["h0"], I["layers"], I["g_final"], I["w_lm"], I["k_caches"],
+                              I["v_caches"], L, parent, Hq, Hkv, dh, dtype)
+    for b in range(B):
+        ref = _causal_forward(I["h0"][b], int(L[b]), I["layers"], I["g_final"], I["w_lm"],
+                              I["k_caches"], I["v_caches"], Hq, Hkv, dh, dtype, b)
+        np.testing.assert_allclose(o["logits"][b], ref, rtol=1e-9, atol=1e-9)
+
+
+def test_forward_each_node_is_its_path_decoded():
+    """A branching tree: every node's logits equal causal decoding of its
+    root -> node path."""
+    dtype = "f32"
+    B, d, Hq, Hkv, dh, V, Lcap, N = 1, 32, 2, 1, 16, 30, 9, 3
+    t = W.full_product_tree(2, 2)                     # 7 nodes
+    I = _fwd_inputs(12, B, t.T, d, Hq, Hkv, dh, V, Lcap, N, dtype)
+    o = oracle.verify_forward(I["h0"], I["layers"], I["g_final"], I["w_lm"], I["k_caches"],
+                              I["v_caches"], [7], t.parent, Hq, Hkv, dh, dtype)
+    for n in range(t.T):
+        path = []
+        a = n
+        while a != -1:
+            path.append(a)
+            a = int(t.parent[a])
+        path = path[::-1]
+        ref = _causal_forward(I["h0"][0, path], 7, I["layers"], I["g_final"], I["w_lm"],
+                              I["k_caches"], I["v_caches"], Hq, Hkv, dh, dtype, 0)
+        np.testing.assert_allclose(o["logits"][0, n], ref[-1], rtol=1e-9, atol=1e-9)
+
+
+def test_forward_without_layers_is_the_lm_head():
+    I = _fwd_inputs(13, 1, 3, 32, 2, 2, 16, 20, 4, 0, "f32")
+    o = oracle.verify_forward(I["h0"], [], I["g_final"], I["w_lm"], [np.zeros((1, 2, 4, 16), np.float32)],
+                              [], [4], [-1, 0, 0], 2, 2, 16, "f32")
+    h = oracle.decode(I["h0"], "f32")[0]
+    x = oracle.round_to(oracle.rmsnorm(h, 1.0, 1e-6), "f32")      # the one rounding point
+    np.testing.assert_allclose(o["logits"][0], x @ oracle.decode(I["w_lm"], "f32").T, rtol=1e-12)
