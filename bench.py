@@ -40,6 +40,8 @@ def parse():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle timing")
+    ap.add_argument("--forward-blocks", type=int, default=4,
+                    help="attention blocks of the synthetic verify forward (a next-row timing)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -257,6 +259,8 @@ def main():
                                            wl.temperature if wl.mode != "greedy" else 1.0,
                                            token=samp), args.steps,
             B * V * (2 if wl.dtype == W.BF16 else 4)),          # the best rows, read once
+        "verify_forward": measure_forward(mv, wl, tree, plen, ax["prefix_len"], args.steps,
+                                          args.forward_blocks),
     }
 
     if not args.no_cpu_baseline:
@@ -310,6 +314,45 @@ def measure_commit(mv, wl, tree, kc, vc, kt, vt, plen, best_node, steps):
     nbytes = 2 * 2 * Hkv * rows * dh * w          # K and V rows: read from the tree, written to the cache
     return {"us": round(us, 2), "rows": rows, "bytes": nbytes,
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 2)}
+
+
+def measure_forward(mv, wl, tree, plen, plen_np, steps, N):
+    """The multi-block synthetic verify forward (logits of every tree node
+    from N attention blocks + the LM head) on its own.  Random-init weights
+    and caches of the workload's shape, generated on the device, every block
+    with its own weights and caches (nothing is re-read from a cache that a
+    previous block warmed).  Bytes: weights, the cached prefix keys/values
+    of every block, and the logits written once."""
+    import torch
+    dev = plen.device
+    dt = torch.bfloat16 if wl.dtype == W.BF16 else torch.float32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * wl.cid + 17)
+    B, T, d, V, Hq, Hkv, dh = wl.B, wl.T, wl.d, wl.V, wl.Hq, wl.Hkv, wl.dh
+
+    def rnd(shape, std, mean=0.0):
+        return (torch.randn(shape, generator=gen, device=dev) * std + mean).to(dt)
+
+    layers = [{"g": rnd((d,), 0.1, 1.0), "wq": rnd((Hq * dh, d), d ** -0.5),
+               "wk": rnd((Hkv * dh, d), d ** -0.5), "wv": rnd((Hkv * dh, d), d ** -0.5),
+               "wo": rnd((d, Hq * dh), (Hq * dh) ** -0.5)} for _ in range(N)]
+    kcs = [rnd((B, Hkv, wl.Lcap, dh), 1.0) for _ in range(N)]
+    vcs = [rnd((B, Hkv, wl.Lcap, dh), 1.0) for _ in range(N)]
+    h0, g_final, w_lm = rnd((B, T, d), 1.0), rnd((d,), 0.1, 1.0), rnd((V, d), 0.02)
+    ws = mv.workspace(mv.lib.medusa_verify_forward_workspace_bytes(B, T, d, Hq, Hkv, dh, wl.Lcap,
+                                                                   V, mv.BF16 if dt == torch.bfloat16
+                                                                   else mv.F32), dev)
+    out = {"logits": torch.empty((B, T, V), dtype=torch.float32, device=dev)}
+    w = 2 if dt == torch.bfloat16 else 4
+    Ltot = int(np.minimum(plen_np, wl.Lcap).sum())
+    nbytes = (N * ((2 * Hq + 2 * Hkv) * dh * d * w + 2 * Hkv * Ltot * dh * w)
+              + V * d * w + B * T * V * 4)
+    r = time_call(lambda: mv.medusa_verify_forward(h0, layers, g_final, w_lm, kcs, vcs, plen,
+                                                   tree.parent, Hq, Hkv, dh, ws=ws, out=out),
+                  steps, nbytes)
+    r["blocks"] = N
+    del layers, kcs, vcs
+    return r
 
 
 def cpu_baseline(wl, hx, ax, tree, cand, vlog_np, budget_s):

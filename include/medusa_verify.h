@@ -14,6 +14,8 @@
  *   tree_accept        greedy or typical acceptance of the longest valid path
  *   medusa_sample_token a sampled bonus token from the best node's row
  *   tree_commit_kv     append the accepted path's K/V rows to the cache
+ *   medusa_verify_forward  N attention blocks + LM head over the tree's
+ *                      tokens: verification logits from a forward pass
  *
  * Conventions (all calls):
  *  - Every pointer marked "device" is device memory on the current HIP
@@ -69,6 +71,7 @@ typedef enum {
 #define MEDUSA_MAX_HEADS 16     /* K                                      */
 #define MEDUSA_MAX_TOPS 8       /* s                                      */
 #define MEDUSA_MAX_TREE 256     /* T, nodes including the root            */
+#define MEDUSA_MAX_LAYERS 256   /* N, attention blocks of the forward      */
 
 /* ------------------------------------------------------------------------
  * medusa_heads_topk -- the K Medusa heads and their top-s candidates.
@@ -276,6 +279,58 @@ const char *medusa_status_str(int status);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int medusa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * medusa_verify_forward -- the tree's verification logits from a forward
+ * pass of N attention blocks and the LM head.
+ *
+ * Tree-attention section of the paper explainer page: all candidates are
+ * verified in one forward pass under the tree mask; page
+ * "Medusa：基于多Token预测的LLM推理加速", section 5.3, flattens the tree into
+ * one sequence, runs the model once and reads the logits of every position.
+ * The blocks here are attention-only (no MLP), pre-norm, without biases:
+ *   x = rmsnorm(h) g_l (rounded to dtype), rmsnorm(h) = h / sqrt(mean(h^2) + eps)
+ *   q = rope(x Wq_l^T), k = rope(x Wk_l^T), v = x Wv_l^T   (rounded to dtype)
+ *   o = tree_attention(q, k_cache_l, v_cache_l, k, v) with scale 1/sqrt(dh)
+ *   h = h + o Wo_l^T                                       (fp32)
+ *   logits = (rmsnorm(h) g_final, rounded) W_lm^T          (fp32)
+ * h starts as h0 (the tree tokens' embeddings).  rope rotates the pairs
+ * (j, j + dh/2) of every head by pos * theta^(-2j/dh) with
+ * pos = clamp(prefix_len[b], 0, Lcap) + depth(n): a node follows its
+ * ancestors.  The caches hold keys already rotated at their positions.
+ *
+ *   h0          device [B][T][d] dtype
+ *   g, wq, wk, wv, wo
+ *               host arrays [N] of device pointers: g_l [d], wq_l [Hq*dh][d],
+ *               wk_l and wv_l [Hkv*dh][d], wo_l [d][Hq*dh] (dtype, [out][in])
+ *   g_final     device [d] dtype;  w_lm  device [V][d] dtype
+ *   k_caches, v_caches
+ *               host arrays [N] of device pointers, each [B][Hkv][Lcap][dh]
+ *   prefix_len  device [B] int32 (as tree_attention); parent host [T] int32
+ *   logits      device [B][T][V] float32
+ *   hidden_out  device [B][T][d] float32 or NULL: h after the last block
+ *   k_tree_out, v_tree_out
+ *               device [N][B][Hkv][T][dh] dtype or NULL: every block's tree
+ *               keys (rotated) and values, ready for tree_commit_kv
+ *
+ * Limits: 0 <= N <= 256, T <= 256, dh in {64, 128}, Hq % Hkv == 0,
+ * d % 32 == 0 (BF16) or d % 16 == 0 (F32), B*T*V < 2^31, theta > 0,
+ * eps >= 0.  Arithmetic: MFMA with fp32 accumulation, partial sums added
+ * in a fixed order (results do not vary from run to run); rotary angles
+ * in fp64.  Several kernels per block; the tree attention is the one
+ * tree_attention runs.
+ * ---------------------------------------------------------------------- */
+int medusa_verify_forward(const void *h0, int N, const void *const *g, const void *const *wq,
+                          const void *const *wk, const void *const *wv, const void *const *wo,
+                          const void *g_final, const void *w_lm, const void *const *k_caches,
+                          const void *const *v_caches, const int32_t *prefix_len,
+                          const int32_t *parent, int B, int T, int d, int Hq, int Hkv, int dh,
+                          int Lcap, int V, int dtype, double theta, float eps, float *logits,
+                          float *hidden_out, void *k_tree_out, void *v_tree_out, void *ws,
+                          size_t ws_bytes, void *stream);
+
+size_t medusa_verify_forward_workspace_bytes(int B, int T, int d, int Hq, int Hkv, int dh,
+                                             int Lcap, int V, int dtype);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
            "medusa_heads_stage2",
            "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
            "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
-           "medusa_status_str",
+           "medusa_verify_forward", "medusa_verify_forward_workspace_bytes", "medusa_status_str",
            "medusa_abi_version"]
 
 
@@ -59,12 +59,17 @@ def _load() -> ctypes.CDLL:
     L.tree_accept_workspace_bytes.restype = Z
     L.tree_commit_kv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
     L.medusa_sample_token.argtypes = [P, P, P, I, I, I, I, F, P, P]
+    D = ctypes.c_double
+    L.medusa_verify_forward.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                        I, I, D, F, P, P, P, P, P, Z, P]
+    L.medusa_verify_forward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+    L.medusa_verify_forward_workspace_bytes.restype = Z
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
     for f in ("medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
               "medusa_heads_stage2", "tree_attention",
-              "tree_accept", "tree_commit_kv", "medusa_sample_token"):
+              "tree_accept", "tree_commit_kv", "medusa_sample_token", "medusa_verify_forward"):
         getattr(L, f).restype = I
     return L
 
@@ -264,4 +269,53 @@ def medusa_heads_topk_root(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Ten
                                     _ptr(out["root_token"]), _ptr(out["root_val"]), _ptr(ws),
                                     ws.numel(), _stream(stream))
     _check("medusa_heads_topk_root", rc)
+    return out
+
+
+def _ptr_array(ts: Sequence[torch.Tensor], name: str):
+    for i, t in enumerate(ts):
+        _need(t, f"{name}[{i}]")
+    arr = (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+    return arr
+
+
+def medusa_verify_forward(h0: torch.Tensor, layers: Sequence[Dict[str, torch.Tensor]],
+                          g_final: torch.Tensor, w_lm: torch.Tensor,
+                          k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
+                          prefix_len: torch.Tensor, parent, Hq: int, Hkv: int, dh: int, *,
+                          theta: float = 10000.0, eps: float = 1e-6, want_hidden: bool = False,
+                          want_kv: bool = False, ws: Optional[torch.Tensor] = None,
+                          out: Optional[Dict[str, torch.Tensor]] = None,
+                          stream=None) -> Dict[str, torch.Tensor]:
+    """Logits [B][T][V] (float32) of the tree tokens from N attention blocks
+    (layers: dicts with g, wq, wk, wv, wo) and the LM head; optionally the
+    final residual stream (hidden) and every block's tree k/v."""
+    for t, n in ((h0, "h0"), (g_final, "g_final"), (w_lm, "w_lm"), (prefix_len, "prefix_len")):
+        _need(t, n)
+    B, T, d = h0.shape
+    V = w_lm.shape[0]
+    N = len(layers)
+    Lcap = k_caches[0].shape[2] if N else 0
+    dt = _dtype_code(h0)
+    dev = h0.device
+    par, par_p = _host_i32(parent)
+    arrs = {k: _ptr_array([lw[k] for lw in layers], k) for k in ("g", "wq", "wk", "wv", "wo")}
+    kc = _ptr_array(list(k_caches), "k_caches")
+    vc = _ptr_array(list(v_caches), "v_caches")
+    if out is None:
+        out = {"logits": torch.empty((B, T, V), dtype=torch.float32, device=dev)}
+        if want_hidden:
+            out["hidden"] = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+        if want_kv and N:
+            out["k_tree"] = torch.empty((N, B, Hkv, T, dh), dtype=h0.dtype, device=dev)
+            out["v_tree"] = torch.empty((N, B, Hkv, T, dh), dtype=h0.dtype, device=dev)
+    if ws is None:
+        ws = workspace(lib.medusa_verify_forward_workspace_bytes(B, T, d, Hq, Hkv, dh, Lcap, V, dt),
+                       dev)
+    rc = lib.medusa_verify_forward(
+        _ptr(h0), N, arrs["g"], arrs["wq"], arrs["wk"], arrs["wv"], arrs["wo"], _ptr(g_final),
+        _ptr(w_lm), kc, vc, _ptr(prefix_len), par_p, B, T, d, Hq, Hkv, dh, Lcap, V, dt,
+        float(theta), float(eps), _ptr(out["logits"]), _ptr(out.get("hidden")),
+        _ptr(out.get("k_tree")), _ptr(out.get("v_tree")), _ptr(ws), ws.numel(), _stream(stream))
+    _check("medusa_verify_forward", rc)
     return out

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmedusa_verify.so")
-SOURCES = ["heads.hip", "tree_attention.hip", "tree_accept.hip", "tree_commit.hip"]
+SOURCES = ["heads.hip", "tree_attention.hip", "tree_accept.hip", "tree_commit.hip", "forward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -18,7 +18,10 @@ generated in parallel chunks of CHUNK elements with a result that does not
 depend on the thread count.  Stream ids:
  1 hidden, 2 W1, 3 W2, 4 q, 5 k_cache, 6 v_cache, 7 k_tree, 8 v_tree,
  9 prefix lengths, 10 verification logits (noise), 11 planting decisions,
- 12 synthetic candidate-id table.
+ 12 synthetic candidate-id table, 13 sampling uniforms, 14 LM head,
+ 15 tree-token embeddings h0, 16 final norm gain, and for the forward's
+ block l: 200 + 8l + j with j = 0 gain, 1 Wq, 2 Wk, 3 Wv, 4 Wo, 5 k cache,
+ 6 v cache (l < 100).
 bf16 tensors are drawn in fp32 and rounded to bf16 (round-to-nearest-even)
 and are returned as uint16 bit patterns.
 """
@@ -387,3 +390,42 @@ def verify_logits(wl: Workload, tree: Tree, tokens: np.ndarray,
                 if n not in kids:
                     noise[b, n] *= np.float32(tau)
     return encode(noise, wl.dtype) if wl.dtype == BF16 else noise
+
+
+def forward_inputs(wl: Workload, N: int, T: Optional[int] = None,
+                   seed_base: Optional[int] = None) -> Dict[str, object]:
+    """Random-init weights and caches of N pre-norm attention blocks of the
+    workload's shape plus its LM head, and embeddings h0 [B][T][d] of the
+    tree tokens.  Projections ~ N(0, 1/fan_in), norm gains ~ N(1, 0.1^2),
+    LM head ~ N(0, 0.02^2) (the heads' weight scale), h0 and the caches
+    (keys taken as already rotated) ~ N(0, 1)."""
+    if N > 100:
+        raise ValueError("at most 100 blocks have their own seed streams")
+    base = 1000 * wl.cid if seed_base is None else seed_base
+    T = wl.T if T is None else T
+    B, d, Hq, Hkv, dh, dt = wl.B, wl.d, wl.Hq, wl.Hkv, wl.dh, wl.dtype
+
+    def gain(seed: int) -> np.ndarray:
+        return encode(1.0 + normal_tensor(seed, (d,), 0.1, F32), dt)
+
+    layers = []
+    for l in range(N):
+        sb = base + 200 + 8 * l
+        layers.append({
+            "g": gain(sb),
+            "wq": normal_tensor(sb + 1, (Hq * dh, d), float(1 / np.sqrt(d)), dt),
+            "wk": normal_tensor(sb + 2, (Hkv * dh, d), float(1 / np.sqrt(d)), dt),
+            "wv": normal_tensor(sb + 3, (Hkv * dh, d), float(1 / np.sqrt(d)), dt),
+            "wo": normal_tensor(sb + 4, (d, Hq * dh), float(1 / np.sqrt(Hq * dh)), dt),
+        })
+    return {
+        "h0": normal_tensor(base + 15, (B, T, d), 1.0, dt),
+        "layers": layers,
+        "g_final": gain(base + 16),
+        "w_lm": normal_tensor(base + 14, (wl.V, d), 0.02, dt),
+        "k_caches": [normal_tensor(base + 205 + 8 * l, (B, Hkv, wl.Lcap, dh), 1.0, dt)
+                     for l in range(N)],
+        "v_caches": [normal_tensor(base + 206 + 8 * l, (B, Hkv, wl.Lcap, dh), 1.0, dt)
+                     for l in range(N)],
+        "prefix_len": prefix_lengths(wl, base),
+    }

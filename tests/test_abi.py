@@ -148,3 +148,34 @@ def test_sample_validation(mv):
     assert call(dt=2) == -3
     assert call(B=0) == -2 and call(T=0) == -2 and call(V=0) == -2
     assert call(temp=0.0) == -6 and call(temp=-1.0) == -6 and call(temp=float("inf")) == -6
+
+
+def test_forward_validation(mv):
+    L = mv.lib
+    ok = dict(N=2, B=1, T=4, d=256, Hq=4, Hkv=2, dh=64, Lcap=128, V=1000, dt=1)
+    par = _i32([-1, 0, 0, 1])
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    holes = (ctypes.c_void_p * 2)(0x1000, None)
+
+    def call(h0=FAKE, g=ptrs, wq=ptrs, kc=ptrs, parent=par, logits=FAKE, ws=FAKE_WS, wsb=1 << 40,
+             theta=10000.0, eps=1e-6, **kw):
+        a = dict(ok, **kw)
+        return L.medusa_verify_forward(h0, a["N"], g, wq, ptrs, ptrs, ptrs, FAKE, FAKE, kc, ptrs,
+                                       FAKE, parent, a["B"], a["T"], a["d"], a["Hq"], a["Hkv"],
+                                       a["dh"], a["Lcap"], a["V"], a["dt"], theta, eps, logits,
+                                       None, None, None, ws, wsb, None)
+    assert call(h0=None) == -1 and call(logits=None) == -1
+    assert call(g=None) == -1 and call(wq=holes) == -1 and call(kc=holes) == -1
+    assert call(dt=5) == -3
+    assert call(N=-1) == -2 and call(N=257) == -2 and call(B=0) == -2 and call(T=257) == -2
+    assert call(d=100) == -2 and call(d=16) == -2 and call(dh=96) == -2 and call(Hkv=3) == -2
+    assert call(V=0) == -2 and call(B=64, T=256, V=200000) == -2
+    assert call(dt=0, d=16, wsb=64) == -5       # fp32 takes d % 16 == 0 (fails later, on ws)
+    assert call(theta=0.0) == -6 and call(theta=float("inf")) == -6 and call(eps=-1.0) == -6
+    assert call(parent=_i32([0, 0, 0, 1])) == -4 and call(parent=_i32([-1, 0, 2, 1])) == -4
+    assert call(ws=None) == -5 and call(ws=ctypes.c_void_p(0x10010)) == -5 and call(wsb=64) == -5
+    # zero blocks: only the final norm and the LM head; the block arrays may be NULL
+    assert call(N=0, g=None, wq=None, kc=None, ws=None) == -5
+    ws = L.medusa_verify_forward_workspace_bytes(1, 4, 256, 4, 2, 64, 128, 1000, 1)
+    assert ws >= 4 * 256 * 4                     # the fp32 residual stream at least
+    assert L.medusa_verify_forward_workspace_bytes(1, 4, 100, 4, 2, 64, 128, 1000, 1) == 0
