@@ -15,12 +15,14 @@
 // The projections are skinny GEMMs Y[M][N] = X[M][K] W[N][K]^T with
 // M = B*T tree rows: W is streamed from HBM once (per 64 rows of X) as the
 // A operand of 16x16 MFMA tiles and X, small and L2-resident, is the B
-// operand.  A workgroup owns 64 rows of W and a slice of K; its four waves
-// split that slice and are summed in LDS in a fixed order; S workgroups
-// per 64-row block split K further and leave fp32 partials that an
+// operand.  With M > 16, X is staged through LDS once per workgroup of 128
+// W rows and shared by its four waves, so that X costs few load
+// instructions per W byte (the load path, not HBM, limits otherwise).  S
+// workgroups per row block may split K; they leave fp32 partials that an
 // epilogue kernel sums in a fixed order, so results do not depend on
-// timing.  The q/k/v epilogue also applies the rotary embedding and writes
-// the [B][H][T][dh] layout the tree attention reads; the output projection
+// timing.  The q/k/v epilogue also applies the rotary embedding (from a
+// per-call fp64 table of cos/sin at every node's position) and writes the
+// [B][H][T][dh] layout the tree attention reads; the output projection
 // reads the attention output in that layout directly.
 #include <math.h>
 
@@ -37,27 +39,66 @@ extern "C" size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lca
 namespace medusa {
 namespace {
 
+// Streaming kernel (any K, small M): waves split K.
 constexpr int kGemmWaves = 4;       // waves per workgroup, each a slice of the WG's K range
 constexpr int kGemmTiles = 4;       // 16-row W tiles per workgroup
 constexpr int kGemmRows = 16 * kGemmTiles;
 constexpr int kGemmCols = 64;       // X rows per workgroup (MT <= 4 tiles of 16)
 constexpr int kGemmUnroll = 4;      // k-steps per batch of loads
-constexpr int kGemmTargetWaves = 8 * kNumCU;
+// Staged kernel (K a multiple of one stage, 32 < M): X through LDS.
+constexpr int kLdsWaves = 4;
+constexpr int kLdsTW = 2;           // 16-row W tiles per wave
+constexpr int kLdsRows = kLdsWaves * kLdsTW * 16;
+constexpr int kLdsU = 4;            // k-steps per stage
+constexpr int kMaxSplit = 8;        // K splits (partials) per row block
 constexpr int kEpiThreads = 256;
 constexpr int kNormThreads = 256;
 
 struct GemmArgs {
     const void *X;        // [M][K], or [B][H][T][dh] with K = H * dh when xT > 0
     const void *W0, *W1, *W2;   // row segments of W, concatenated
-    int end0, end1;       // first row of segments 1 and 2 (multiples of kGemmRows)
+    int end0, end1;       // first row of segments 1 and 2 (multiples of 64)
     float *Y;             // direct: [M][N]; otherwise partials [S][M][N]
     int M, N, K, S, MG;
     int xT, xsh;          // heads layout of X: T and log2(dh)
     int direct, accumulate;
 };
 
-// One workgroup: W rows [n0, n0 + 64) x X rows [m0, m0 + 16 MT) over the
-// k-steps of split s.  Wave w takes the w-th quarter of those k-steps.
+// Offset of element k of an X row: plain rows, or the [B][H][T][dh] layout
+// (row base at head 0; head k >> xsh sits xT rows of dh further on).
+__device__ __forceinline__ int x_off(int k, int xT, int xsh) {
+    return xT > 0 ? (((k >> xsh) * xT) << xsh) + (k & ((1 << xsh) - 1)) : k;
+}
+
+template <typename T>
+__device__ __forceinline__ const T *x_row(const GemmArgs &a, int m) {
+    if (a.xT > 0) {
+        const int b = m / a.xT, t = m - b * a.xT;
+        return (const T *)a.X + ((size_t)b * (a.K >> a.xsh) * a.xT + t) * ((size_t)1 << a.xsh);
+    }
+    return (const T *)a.X + (size_t)m * a.K;
+}
+
+// Writes a lane's 4 outputs Y[m][n .. n + 3] (direct, optionally added to
+// Y) or the partial of split s.
+__device__ __forceinline__ void gemm_store(const GemmArgs &a, int s, int m, int n, f32x4 v) {
+    if (m >= a.M || n >= a.N) return;
+    float *dst = (a.direct ? a.Y : a.Y + (size_t)s * a.M * a.N) + (size_t)m * a.N + n;
+    if ((a.N & 3) == 0) {
+        if (a.accumulate) v += *reinterpret_cast<const f32x4 *>(dst);
+        *reinterpret_cast<f32x4 *>(dst) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (n + i < a.N) dst[i] = (a.accumulate ? dst[i] : 0.f) + v[i];
+    }
+}
+
+// Streaming kernel.  One workgroup: W rows [n0, n0 + 64) x X rows
+// [m0, m0 + 16 MT) over the k-steps of split s; wave w takes the w-th
+// quarter of them in whole batches of kGemmUnroll (the last part also the
+// remainder).  Every batch issues all its loads before its MFMAs; the four
+// waves' sums are added in LDS as (w0 + w2) + (w1 + w3).
 template <typename T, int MT>
 __global__ __launch_bounds__(kGemmWaves *kWave) void gemm_xwt_kernel(GemmArgs a) {
     constexpr int KC = Elem<T>::kPer16B;
@@ -78,8 +119,10 @@ __global__ __launch_bounds__(kGemmWaves *kWave) void gemm_xwt_kernel(GemmArgs a)
     const T *W = (const T *)(n0 >= a.end1 ? a.W2 : (n0 >= a.end0 ? a.W1 : a.W0));
     const int segbeg = n0 >= a.end1 ? a.end1 : (n0 >= a.end0 ? a.end0 : 0);
 
-    const int KS = K / KSTEP, parts = a.S * kGemmWaves, part = s * kGemmWaves + wave;
-    const int kb = (int)((long long)KS * part / parts), ke = (int)((long long)KS * (part + 1) / parts);
+    const int KS = K / KSTEP, NB = KS / U, parts = a.S * kGemmWaves, part = s * kGemmWaves + wave;
+    const int kb = (int)((long long)NB * part / parts) * U;
+    const int kbe = (int)((long long)NB * (part + 1) / parts) * U;
+    const int ke = part == parts - 1 ? KS : kbe;
 
     const T *arow[kGemmTiles];
 #pragma unroll
@@ -88,18 +131,12 @@ __global__ __launch_bounds__(kGemmWaves *kWave) void gemm_xwt_kernel(GemmArgs a)
         n = n < N ? n : N - 1;
         arow[r] = W + (size_t)(n - segbeg) * K + g * KC;
     }
-    const int xT = a.xT, xsh = a.xsh, xmask = (1 << xsh) - 1;
+    const int xT = a.xT, xsh = a.xsh;
     const T *brow[MT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
         int m = m0 + 16 * j + c;
-        m = m < M ? m : M - 1;
-        if (xT > 0) {
-            const int b = m / xT, t = m - b * xT;
-            brow[j] = (const T *)a.X + ((size_t)b * (K >> xsh) * xT + t) * ((size_t)1 << xsh) + g * KC;
-        } else {
-            brow[j] = (const T *)a.X + (size_t)m * K + g * KC;
-        }
+        brow[j] = x_row<T>(a, m < M ? m : M - 1) + g * KC;
     }
 
     f32x4 acc[kGemmTiles][MT];
@@ -108,29 +145,39 @@ __global__ __launch_bounds__(kGemmWaves *kWave) void gemm_xwt_kernel(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < MT; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k = kb; k < ke; k += U) {
-        // a short last batch loads its final step again (cached) and skips
-        // the extra products, so every batch issues all its loads up front
-        const int nu = ke - k < U ? ke - k : U;
+    int k = kb;
+    for (; k < kbe; k += U) {
         u32x4 av[kGemmTiles][U], bv[MT][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int kk = (k + (u < nu ? u : nu - 1)) * KSTEP;
-            const size_t xo = xT > 0 ? ((size_t)(kk >> xsh) * xT << xsh) + (kk & xmask) : (size_t)kk;
+            const int kk = (k + u) * KSTEP;
+            const int xo = x_off(kk, xT, xsh);
 #pragma unroll
             for (int j = 0; j < MT; ++j) bv[j][u] = ld16(brow[j] + xo);
 #pragma unroll
             for (int r = 0; r < kGemmTiles; ++r) av[r][u] = ld16(arow[r] + kk);
         }
+        // keep the whole batch of loads ahead of the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u < nu) {
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int r = 0; r < kGemmTiles; ++r)
+            for (int r = 0; r < kGemmTiles; ++r)
 #pragma unroll
-                    for (int j = 0; j < MT; ++j) mma16_step(acc[r][j], av[r][u], bv[j][u], T{});
-            }
-        }
+                for (int j = 0; j < MT; ++j) mma16_step(acc[r][j], av[r][u], bv[j][u], T{});
+    }
+    for (; k < ke; ++k) {
+        const int kk = k * KSTEP;
+        const int xo = x_off(kk, xT, xsh);
+        u32x4 av[kGemmTiles], bv[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) bv[j] = ld16(brow[j] + xo);
+#pragma unroll
+        for (int r = 0; r < kGemmTiles; ++r) av[r] = ld16(arow[r] + kk);
+#pragma unroll
+        for (int r = 0; r < kGemmTiles; ++r)
+#pragma unroll
+            for (int j = 0; j < MT; ++j) mma16_step(acc[r][j], av[r], bv[j], T{});
     }
 
     // (w0 + w2) + (w1 + w3); wave 0 finishes tiles 0-1, wave 1 tiles 2-3
@@ -157,83 +204,245 @@ __global__ __launch_bounds__(kGemmWaves *kWave) void gemm_xwt_kernel(GemmArgs a)
     }
     __syncthreads();
     if (wave >= 2) return;
-    float *Y = a.direct ? a.Y : a.Y + (size_t)s * M * N;
-    const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int r = 0; r < kGemmTiles; ++r) {
         if ((r < kGemmTiles / 2) != (wave == 0)) continue;
-        const int n = n0 + 16 * r + 4 * g;   // lane holds Y[m0 + 16j + c][n .. n + 3]
+#pragma unroll
+        for (int j = 0; j < MT; ++j)   // lane holds Y[m0 + 16j + c][n0 + 16r + 4g .. + 3]
+            gemm_store(a, s, m0 + 16 * j + c, n0 + 16 * r + 4 * g,
+                       acc[r][j] + red[1 - wave][r * MT + j][lane]);
+    }
+}
+
+// ---- staged kernel
+template <typename T, int MT>
+struct LdsCfg {
+    static constexpr int KC = Elem<T>::kPer16B;
+    static constexpr int KSTEP = 4 * KC;
+    static constexpr int SK = kLdsU * KSTEP;                           // k per stage
+    static constexpr int CHUNKS = kLdsU * MT * kWave;                  // 16-B X chunks per stage
+    static constexpr int XPT = CHUNKS / (kLdsWaves * kWave);           // per thread
+    static_assert(CHUNKS % (kLdsWaves * kWave) == 0, "X stage split");
+};
+
+// Issue one stage's loads: this thread's X chunks first (they are waited
+// for first, to be stored to LDS), then this wave's W tiles.
+template <typename T, int MT, int XPT>
+__device__ __forceinline__ void lds_load_stage(u32x4 (&w)[kLdsTW][kLdsU], u32x4 (&xr)[XPT],
+                                               const T *const (&arow)[kLdsTW],
+                                               const T *const (&xrow)[XPT], const int (&koff)[XPT],
+                                               int k0, int xT, int xsh) {
+    constexpr int KSTEP = LdsCfg<T, MT>::KSTEP;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xr[i] = ld16(xrow[i] + x_off(k0 + koff[i], xT, xsh));
+#pragma unroll
+    for (int u = 0; u < kLdsU; ++u)
+#pragma unroll
+        for (int r = 0; r < kLdsTW; ++r) w[r][u] = ld16(arow[r] + k0 + u * KSTEP);
+}
+
+template <typename T, int MT>
+__device__ __forceinline__ void lds_compute_stage(f32x4 (&acc)[kLdsTW][MT],
+                                                  const u32x4 (&w)[kLdsTW][kLdsU],
+                                                  const u32x4 *xs, int lane) {
+#pragma unroll
+    for (int u = 0; u < kLdsU; ++u)
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-            const int m = m0 + 16 * j + c;
-            if (m >= M || n >= N) continue;
-            const f32x4 v = acc[r][j] + red[1 - wave][r * MT + j][lane];
-            float *dst = Y + (size_t)m * N + n;
-            if (vec) {
-                f32x4 o = v;
-                if (a.accumulate) o += *reinterpret_cast<const f32x4 *>(dst);
-                *reinterpret_cast<f32x4 *>(dst) = o;
-            } else {
+            const u32x4 xb = xs[(u * MT + j) * kWave + lane];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (n + i < N) dst[i] = (a.accumulate ? dst[i] : 0.f) + v[i];
+            for (int r = 0; r < kLdsTW; ++r) mma16_step(acc[r][j], w[r][u], xb, T{});
+        }
+}
+
+// Staged kernel.  One workgroup: W rows [n0, n0 + 128) (32 per wave) x X
+// rows [m0, m0 + 16 MT) over the stages of split s.  X's stage (16 MT rows
+// x kLdsU k-steps) is loaded once per workgroup into LDS, already in the
+// MFMA operand order, and read by all four waves; the next stage's X and W
+// loads are issued before the current stage's MFMAs (two LDS buffers, two
+// register sets for W, one barrier per stage).
+template <typename T, int MT>
+__global__ __launch_bounds__(kLdsWaves *kWave, 2) void gemm_lds_kernel(GemmArgs a) {
+    using C = LdsCfg<T, MT>;
+    __shared__ u32x4 xs[2][C::CHUNKS];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane / 16, c = lane % 16;
+    const int lid = (int)xcd_logical_id(blockIdx.x, gridDim.x);
+    const int mg = lid % a.MG, s = (lid / a.MG) % a.S, rb = lid / (a.MG * a.S);
+    const int n0 = rb * kLdsRows + wave * kLdsTW * 16, m0 = mg * kGemmCols;
+    const int M = a.M, N = a.N, K = a.K, xT = a.xT, xsh = a.xsh;
+    // the segment of this wave's rows; a wave wholly past N (N not a
+    // multiple of 32) reads row N - 1 of the last segment, never before it
+    const int nsel = n0 < N ? n0 : N - 1;
+    const T *W = (const T *)(nsel >= a.end1 ? a.W2 : (nsel >= a.end0 ? a.W1 : a.W0));
+    const int segbeg = nsel >= a.end1 ? a.end1 : (nsel >= a.end0 ? a.end0 : 0);
+    const int NST = K / C::SK;
+    const int sb = NST * s / a.S, se = NST * (s + 1) / a.S;
+
+    const T *arow[kLdsTW];
+#pragma unroll
+    for (int r = 0; r < kLdsTW; ++r) {
+        int n = n0 + 16 * r + c;
+        n = n < N ? n : N - 1;
+        arow[r] = W + (size_t)(n - segbeg) * K + g * C::KC;
+    }
+    // X chunk q = tid + i * 256 of a stage: k-step u, column tile j, lane l
+    const T *xrow[C::XPT];
+    int koff[C::XPT];
+#pragma unroll
+    for (int i = 0; i < C::XPT; ++i) {
+        const int q = tid + i * kLdsWaves * kWave;
+        const int l = q % kWave, j = (q / kWave) % MT, u = q / (kWave * MT);
+        const int m = m0 + 16 * j + l % 16;
+        xrow[i] = x_row<T>(a, m < M ? m : M - 1);
+        koff[i] = u * C::KSTEP + (l / 16) * C::KC;
+    }
+    f32x4 acc[kLdsTW][MT];
+#pragma unroll
+    for (int r = 0; r < kLdsTW; ++r)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (sb < se) {
+        u32x4 wa[kLdsTW][kLdsU], wb[kLdsTW][kLdsU], xr[C::XPT];
+        lds_load_stage<T, MT, C::XPT>(wa, xr, arow, xrow, koff, sb * C::SK, xT, xsh);
+#pragma unroll
+        for (int i = 0; i < C::XPT; ++i) xs[0][tid + i * kLdsWaves * kWave] = xr[i];
+        __syncthreads();
+        int st = sb, buf = 0;
+        // stages alternate between the W register sets wa and wb
+        while (true) {
+            if (st + 1 < se) {
+                lds_load_stage<T, MT, C::XPT>(wb, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_compute_stage<T, MT>(acc, wa, xs[buf], lane);
+#pragma unroll
+                for (int i = 0; i < C::XPT; ++i) xs[buf ^ 1][tid + i * kLdsWaves * kWave] = xr[i];
+                __syncthreads();
+            } else {
+                lds_compute_stage<T, MT>(acc, wa, xs[buf], lane);
+                break;
             }
+            ++st;
+            buf ^= 1;
+            if (st + 1 < se) {
+                lds_load_stage<T, MT, C::XPT>(wa, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_compute_stage<T, MT>(acc, wb, xs[buf], lane);
+#pragma unroll
+                for (int i = 0; i < C::XPT; ++i) xs[buf ^ 1][tid + i * kLdsWaves * kWave] = xr[i];
+                __syncthreads();
+            } else {
+                lds_compute_stage<T, MT>(acc, wb, xs[buf], lane);
+                break;
+            }
+            ++st;
+            buf ^= 1;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kLdsTW; ++r)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            gemm_store(a, s, m0 + 16 * j + c, n0 + 16 * r + 4 * g, acc[r][j]);
+}
+
+// ---- epilogues
+// Y[i] (+)= sum over s < NS of part[s][i], s in order; four elements per
+// thread when n % 4 == 0.
+template <int NS>
+__global__ __launch_bounds__(kEpiThreads) void epi_sum_kernel(const float *__restrict__ part,
+                                                              float *__restrict__ Y, size_t n,
+                                                              int accumulate) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    if ((n & 3) == 0) {
+        const size_t n4 = n / 4;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+            f32x4 v[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) v[s] = reinterpret_cast<const f32x4 *>(part + s * n)[i];
+            f32x4 t = v[0];
+#pragma unroll
+            for (int s = 1; s < NS; ++s) t += v[s];
+            f32x4 *y = reinterpret_cast<f32x4 *>(Y) + i;
+            *y = accumulate ? *y + t : t;
+        }
+    } else {
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+            float v[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) v[s] = part[s * n + i];
+            float t = v[0];
+#pragma unroll
+            for (int s = 1; s < NS; ++s) t += v[s];
+            Y[i] = accumulate ? Y[i] + t : t;
         }
     }
 }
 
-// Y[i] (+)= sum over s of part[s][i], s in order
-__global__ __launch_bounds__(kEpiThreads) void epi_sum_kernel(const float *__restrict__ part,
-                                                              float *__restrict__ Y, size_t n,
-                                                              int S, int accumulate) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x) {
-        float v = part[i];
-        for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
-        Y[i] = accumulate ? Y[i] + v : v;
+struct RopeTab {
+    const int32_t *prefix_len;
+    double2 *tab;               // [B][T][dh/2]: cos, sin of the rotary angle
+    int B, T, dh, Lcap;
+    double theta;
+    uint8_t depth[MEDUSA_MAX_TREE];
+};
+
+// cos and sin of pos * theta^(-2j/dh) at pos = clamp(L_b, 0, Lcap) + depth(t),
+// in fp64; the same for every block.
+__global__ __launch_bounds__(kEpiThreads) void rope_table_kernel(RopeTab p) {
+    const int half = p.dh / 2, total = p.B * p.T * half;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+        const int j = i % half, t = (i / half) % p.T, b = i / (half * p.T);
+        int L = p.prefix_len[b];
+        L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+        const double ang = (double)(L + p.depth[t]) * pow(p.theta, -2.0 * j / p.dh);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        p.tab[i] = make_double2(cs, sn);
     }
 }
 
 struct QkvEpi {
     const float *part;          // [S][M][N], N = (Hq + 2 Hkv) dh: q | k | v columns
+    const double2 *tab;         // rotary table [M][dh/2]
     void *dst[3];               // q [B][Hq][T][dh], k and v [B][Hkv][T][dh]
-    const int32_t *prefix_len;
-    int S, M, N, T, dh, Hq, Hkv, Lcap;
-    double theta;
-    uint8_t depth[MEDUSA_MAX_TREE];
+    int M, N, T, dh, Hq, Hkv;
 };
 
 // Sum the partials of column pair (j, j + dh/2) of one head, rotate q and k
-// by the angle pos * theta^(-2j/dh) (fp64) at pos = clamp(L_b) + depth(t),
-// round to the dtype and store at [b][h][t][j] and [b][h][t][j + dh/2].
-template <typename T>
+// (x1 cos - x2 sin, x1 sin + x2 cos in fp64), round to the dtype and store
+// at [b][h][t][j] and [b][h][t][j + dh/2].
+template <typename T, int NS>
 __global__ __launch_bounds__(kEpiThreads) void qkv_epi_kernel(QkvEpi p) {
-    const int half = p.dh / 2;
-    const size_t pairs_row = (size_t)p.N / 2, total = (size_t)p.M * pairs_row;
+    const int half = p.dh / 2, pairs_row = p.N / 2, total = p.M * pairs_row;
     const size_t mn = (size_t)p.M * p.N;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (size_t)gridDim.x * blockDim.x) {
-        const int m = (int)(i / pairs_row);
-        const int q = (int)(i - (size_t)m * pairs_row);
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+        const int m = i / pairs_row, q = i - m * pairs_row;
         const int hd = q / half, j = q - hd * half;     // head over q | k | v, pair index
         const int seg = hd < p.Hq ? 0 : (hd < p.Hq + p.Hkv ? 1 : 2);
         const int h = seg == 0 ? hd : (seg == 1 ? hd - p.Hq : hd - p.Hq - p.Hkv);
         const int H = seg == 0 ? p.Hq : p.Hkv;
-        const size_t c1 = (size_t)m * p.N + (size_t)hd * p.dh + j;
-        float x1 = p.part[c1], x2 = p.part[c1 + half];
-        for (int s = 1; s < p.S; ++s) {
-            x1 += p.part[s * mn + c1];
-            x2 += p.part[s * mn + c1 + half];
+        const size_t c1 = (size_t)m * p.N + hd * p.dh + j;
+        float a1[NS], a2[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            a1[s] = p.part[s * mn + c1];
+            a2[s] = p.part[s * mn + c1 + half];
+        }
+        float x1 = a1[0], x2 = a2[0];
+#pragma unroll
+        for (int s = 1; s < NS; ++s) {
+            x1 += a1[s];
+            x2 += a2[s];
         }
         const int b = m / p.T, t = m - b * p.T;
         float y1 = x1, y2 = x2;
         if (seg < 2) {
-            int L = p.prefix_len[b];
-            L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
-            const double ang = (double)(L + p.depth[t]) * pow(p.theta, -2.0 * j / p.dh);
-            const double cs = cos(ang), sn = sin(ang);
-            y1 = (float)((double)x1 * cs - (double)x2 * sn);
-            y2 = (float)((double)x1 * sn + (double)x2 * cs);
+            const double2 cs = p.tab[m * half + j];
+            y1 = (float)((double)x1 * cs.x - (double)x2 * cs.y);
+            y2 = (float)((double)x1 * cs.y + (double)x2 * cs.x);
         }
         T *d = (T *)(seg == 0 ? p.dst[0] : (seg == 1 ? p.dst[1] : p.dst[2])) +
                (((size_t)b * H + h) * p.T + t) * p.dh;
@@ -242,9 +451,37 @@ __global__ __launch_bounds__(kEpiThreads) void qkv_epi_kernel(QkvEpi p) {
     }
 }
 
-// x[m] = rmsnorm(h[m]) g rounded to the dtype, one workgroup per row.  With
-// FROM_IN the row is read from the dtype input (the first block) and also
-// stored to h as fp32, which starts the residual stream.
+// ---- RMSNorm
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T *p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t *p) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+}
+template <typename T>
+__device__ __forceinline__ void store4(T *p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float *p, f32x4 v) {
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 v) {
+    *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+constexpr int kNormU = 4;   // groups of 4 elements per thread per pass step
+
+// x[m] = rmsnorm(h[m]) g rounded to the dtype, one workgroup per row, four
+// elements per thread access with kNormU accesses in flight.  With FROM_IN
+// the row is read from the dtype input (the first block) and also stored to
+// h as fp32, which starts the residual stream.  Every thread reads back only
+// what it wrote itself.
 template <typename T, bool FROM_IN>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const T *__restrict__ in,
                                                                float *__restrict__ h,
@@ -252,16 +489,22 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const T *__restri
                                                                T *__restrict__ x, int d, float eps) {
     __shared__ float red[kNormThreads / kWave];
     const size_t row = (size_t)blockIdx.x * d;
+    const int d4 = d / 4;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < d; i += kNormThreads) {
-        float v;
-        if (FROM_IN) {
-            v = Elem<T>::to_f32(in[row + i]);
-            h[row + i] = v;
-        } else {
-            v = h[row + i];
+    for (int b = 0; b < d4; b += kNormU * kNormThreads) {
+        f32x4 v[kNormU];
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int c4 = b + u * kNormThreads + threadIdx.x;
+            v[u] = c4 < d4 ? (FROM_IN ? load4<T>(in + row + 4 * c4) : load4<float>(h + row + 4 * c4))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        ss += v * v;
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int c4 = b + u * kNormThreads + threadIdx.x;
+            if (FROM_IN && c4 < d4) store4<float>(h + row + 4 * c4, v[u]);
+            ss += v[u][0] * v[u][0] + v[u][1] * v[u][1] + v[u][2] * v[u][2] + v[u][3] * v[u][3];
+        }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
@@ -271,37 +514,62 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const T *__restri
 #pragma unroll
     for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
     const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += kNormThreads) {
-        const float v = FROM_IN ? Elem<T>::to_f32(in[row + i]) : h[row + i];
-        x[row + i] = Elem<T>::from_f32(v * inv * Elem<T>::to_f32(gain[i]));
+    for (int b = 0; b < d4; b += kNormU * kNormThreads) {
+        f32x4 v[kNormU], gv[kNormU];
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int c4 = b + u * kNormThreads + threadIdx.x;
+            const int cc = c4 < d4 ? c4 : d4 - 1;
+            v[u] = load4<float>(h + row + 4 * cc);
+            gv[u] = load4<T>(gain + 4 * cc);
+        }
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int c4 = b + u * kNormThreads + threadIdx.x;
+            if (c4 < d4) store4<T>(x + row + 4 * c4, v[u] * inv * gv[u]);
+        }
     }
 }
 
 // ------------------------------------------------------------------ host
 struct GemmPlan {
+    bool staged;
     int S, MG, RB, MT;
     size_t part_bytes;   // partials needed (0 when written directly)
 };
 
-// S splits of K per 64-row block, so that about kGemmTargetWaves waves run,
-// each with at least two k-steps.  need_part forces partials (an epilogue
-// reads them).
+// The staged kernel when K is a whole number of stages and M > 16 (it pays
+// when X is read by many tiles); else the streaming kernel.  S splits of K
+// per row block when the row blocks alone leave most CUs idle, each split
+// keeping at least four stages (batches per wave); at most kMaxSplit.
+// need_part forces partials (an epilogue reads them).
 inline GemmPlan gemm_plan(int M, int N, int K, int kstep, bool need_part) {
     GemmPlan g;
-    g.RB = (N + kGemmRows - 1) / kGemmRows;
     g.MG = (M + kGemmCols - 1) / kGemmCols;
     g.MT = M >= kGemmCols ? 4 : (M + 15) / 16;
-    const double units = (double)g.RB * g.MG * kGemmWaves;
-    int S = (int)(kGemmTargetWaves / units + 0.5);
-    const int smax = K / kstep / (2 * kGemmWaves);
+    const int KS = K / kstep;
+    g.staged = g.MT >= 2 && KS % kLdsU == 0;
+    int smax, S;
+    if (g.staged) {
+        g.RB = (N + kLdsRows - 1) / kLdsRows;
+        const int units = g.RB * g.MG;
+        S = units >= 3 * kNumCU / 4 ? 1 : (2 * kNumCU + units / 2) / units;
+        smax = KS / kLdsU / 4;
+    } else {
+        g.RB = (N + kGemmRows - 1) / kGemmRows;
+        const int units = g.RB * g.MG;
+        S = units >= 3 * kNumCU / 4 ? 1 : (2 * kNumCU + units / 2) / units;
+        smax = KS / kGemmUnroll / kGemmWaves;
+    }
     S = S < smax ? S : smax;
+    S = S < kMaxSplit ? S : kMaxSplit;
     g.S = S > 1 ? S : 1;
     g.part_bytes = (need_part || g.S > 1) ? (size_t)g.S * M * N * 4 : 0;
     return g;
 }
 
 struct FwdLayout {
-    size_t h, x, q, kt, vt, att, part, attn, total;
+    size_t h, x, q, kt, vt, att, part, tab, attn, total;
     size_t attn_bytes;
     GemmPlan qkv, wo, lm;
 };
@@ -329,6 +597,7 @@ inline FwdLayout fwd_layout(int B, int T, int d, int Hq, int Hkv, int dh, int Lc
     L.vt = take((size_t)M * Hkv * dh * es);
     L.att = take((size_t)M * Hq * dh * es);
     L.part = take(part);
+    L.tab = take((size_t)M * (dh / 2) * sizeof(double2));
     L.attn_bytes = tree_attention_workspace_bytes(B, Hq, Hkv, Lcap, dh, T, dtype);
     L.attn = take(L.attn_bytes);
     L.total = off;
@@ -338,6 +607,23 @@ inline FwdLayout fwd_layout(int B, int T, int d, int Hq, int Hkv, int dh, int Lc
 inline unsigned grid_for(size_t n, int threads) {
     const size_t g = (n + threads - 1) / threads;
     return (unsigned)(g < 8192 ? (g > 0 ? g : 1) : 8192);
+}
+
+template <typename T, int MT>
+void launch_gemm_kernel(const GemmPlan &g, const GemmArgs &a, hipStream_t st) {
+    if (g.staged)
+        hipLaunchKernelGGL((gemm_lds_kernel<T, MT < 2 ? 2 : MT>), dim3((unsigned)(g.RB * g.S * g.MG)),
+                           dim3(kLdsWaves * kWave), 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_xwt_kernel<T, MT>), dim3((unsigned)(g.RB * g.S * g.MG)),
+                           dim3(kGemmWaves * kWave), 0, st, a);
+}
+
+template <int NS>
+void launch_epi_sum(const float *part, float *Y, size_t n, int accumulate, hipStream_t st) {
+    const size_t work = (n & 3) == 0 ? n / 4 : n;
+    hipLaunchKernelGGL(epi_sum_kernel<NS>, dim3(grid_for(work, kEpiThreads)), dim3(kEpiThreads), 0,
+                       st, part, Y, n, accumulate);
 }
 
 // Y (+)= X W^T through the plan: direct when one split and no epilogue,
@@ -350,21 +636,43 @@ int run_gemm(const GemmPlan &g, GemmArgs a, float *Y, float *part, int accumulat
     a.direct = g.part_bytes == 0;
     a.Y = a.direct ? Y : part;
     a.accumulate = a.direct ? accumulate : 0;
-    const dim3 grid((unsigned)(g.RB * g.S * g.MG)), block(kGemmWaves * kWave);
     switch (g.MT) {
-        case 1: hipLaunchKernelGGL((gemm_xwt_kernel<T, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemm_xwt_kernel<T, 2>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemm_xwt_kernel<T, 3>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemm_xwt_kernel<T, 4>), grid, block, 0, st, a); break;
+        case 1: launch_gemm_kernel<T, 1>(g, a, st); break;
+        case 2: launch_gemm_kernel<T, 2>(g, a, st); break;
+        case 3: launch_gemm_kernel<T, 3>(g, a, st); break;
+        default: launch_gemm_kernel<T, 4>(g, a, st); break;
     }
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (!a.direct && epi_sum) {
         const size_t n = (size_t)a.M * a.N;
-        hipLaunchKernelGGL(epi_sum_kernel, dim3(grid_for(n, kEpiThreads)), dim3(kEpiThreads), 0, st,
-                           (const float *)part, Y, n, g.S, accumulate);
+        switch (g.S) {
+            case 1: launch_epi_sum<1>(part, Y, n, accumulate, st); break;
+            case 2: launch_epi_sum<2>(part, Y, n, accumulate, st); break;
+            case 3: launch_epi_sum<3>(part, Y, n, accumulate, st); break;
+            case 4: launch_epi_sum<4>(part, Y, n, accumulate, st); break;
+            case 5: launch_epi_sum<5>(part, Y, n, accumulate, st); break;
+            case 6: launch_epi_sum<6>(part, Y, n, accumulate, st); break;
+            case 7: launch_epi_sum<7>(part, Y, n, accumulate, st); break;
+            default: launch_epi_sum<8>(part, Y, n, accumulate, st); break;
+        }
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     }
     return MEDUSA_OK;
+}
+
+template <typename T>
+void launch_qkv_epi(int S, const QkvEpi &qe, hipStream_t st) {
+    const dim3 grid(grid_for((size_t)qe.M * qe.N / 2, kEpiThreads)), block(kEpiThreads);
+    switch (S) {
+        case 1: hipLaunchKernelGGL((qkv_epi_kernel<T, 1>), grid, block, 0, st, qe); break;
+        case 2: hipLaunchKernelGGL((qkv_epi_kernel<T, 2>), grid, block, 0, st, qe); break;
+        case 3: hipLaunchKernelGGL((qkv_epi_kernel<T, 3>), grid, block, 0, st, qe); break;
+        case 4: hipLaunchKernelGGL((qkv_epi_kernel<T, 4>), grid, block, 0, st, qe); break;
+        case 5: hipLaunchKernelGGL((qkv_epi_kernel<T, 5>), grid, block, 0, st, qe); break;
+        case 6: hipLaunchKernelGGL((qkv_epi_kernel<T, 6>), grid, block, 0, st, qe); break;
+        case 7: hipLaunchKernelGGL((qkv_epi_kernel<T, 7>), grid, block, 0, st, qe); break;
+        default: hipLaunchKernelGGL((qkv_epi_kernel<T, 8>), grid, block, 0, st, qe); break;
+    }
 }
 
 inline GemmArgs gemm_args(const void *X, const void *W, int M, int N, int K) {
@@ -406,20 +714,31 @@ int run_forward(const FwdArgs &f, char *ws, hipStream_t st) {
 
     QkvEpi qe;
     qe.part = part;
-    qe.prefix_len = f.prefix_len;
-    qe.S = L.qkv.S;
+    qe.tab = (const double2 *)(ws + L.tab);
     qe.M = M;
     qe.N = (f.Hq + 2 * f.Hkv) * dh;
     qe.T = f.T;
     qe.dh = dh;
     qe.Hq = f.Hq;
     qe.Hkv = f.Hkv;
-    qe.Lcap = f.Lcap;
-    qe.theta = f.theta;
-    for (int i = 0; i < MEDUSA_MAX_TREE; ++i) qe.depth[i] = 0;
-    for (int n = 1; n < f.T; ++n) qe.depth[n] = (uint8_t)(qe.depth[f.parent[n]] + 1);
     const size_t kv_block = (size_t)M * f.Hkv * dh;   // one block's tree keys (or values)
     const int xsh = dh == 128 ? 7 : 6;
+
+    if (f.N > 0) {
+        RopeTab rt;
+        rt.prefix_len = f.prefix_len;
+        rt.tab = (double2 *)(ws + L.tab);
+        rt.B = f.B;
+        rt.T = f.T;
+        rt.dh = dh;
+        rt.Lcap = f.Lcap;
+        rt.theta = f.theta;
+        for (int i = 0; i < MEDUSA_MAX_TREE; ++i) rt.depth[i] = 0;
+        for (int n = 1; n < f.T; ++n) rt.depth[n] = (uint8_t)(rt.depth[f.parent[n]] + 1);
+        hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)M * dh / 2, kEpiThreads)),
+                           dim3(kEpiThreads), 0, st, rt);
+        if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
+    }
 
     for (int l = 0; l <= f.N; ++l) {
         const T *gain = (const T *)(l < f.N ? f.g[l] : f.g_final);
@@ -441,8 +760,7 @@ int run_forward(const FwdArgs &f, char *ws, hipStream_t st) {
         qe.dst[0] = ws + L.q;
         qe.dst[1] = f.k_tree_out ? (T *)f.k_tree_out + l * kv_block : (T *)(ws + L.kt);
         qe.dst[2] = f.v_tree_out ? (T *)f.v_tree_out + l * kv_block : (T *)(ws + L.vt);
-        hipLaunchKernelGGL(qkv_epi_kernel<T>, dim3(grid_for((size_t)M * qe.N / 2, kEpiThreads)),
-                           dim3(kEpiThreads), 0, st, qe);
+        launch_qkv_epi<T>(L.qkv.S, qe, st);
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
 
         rc = tree_attention(ws + L.q, f.kc[l], f.vc[l], f.prefix_len, qe.dst[1], qe.dst[2],
@@ -473,7 +791,8 @@ static int check_fwd(int N, int B, int T, int d, int Hq, int Hkv, int dh, int Lc
         Lcap < 0 || V < 1)
         return MEDUSA_ERR_SHAPE;
     const long long M = (long long)B * T;
-    if (M * V >= (1LL << 31) || M * d >= (1LL << 31) || (long long)B * Hkv * Lcap * dh >= (1LL << 40))
+    if (M * V >= (1LL << 31) || M * d >= (1LL << 31) || M * (Hq + 2 * Hkv) * dh >= (1LL << 31) ||
+        (long long)B * Hkv * Lcap * dh >= (1LL << 40))
         return MEDUSA_ERR_SHAPE;
     return MEDUSA_OK;
 }
