@@ -696,3 +696,48 @@ def test_forward_without_layers_is_the_lm_head():
     h = oracle.decode(I["h0"], "f32")[0]
     x = oracle.round_to(oracle.rmsnorm(h, 1.0, 1e-6), "f32")      # the one rounding point
     np.testing.assert_allclose(o["logits"][0], x @ oracle.decode(I["w_lm"], "f32").T, rtol=1e-12)
+
+
+def test_forward_zero_output_projection_keeps_the_residual():
+    """Wo = 0: every block adds nothing, so h stays h0 and the logits are the
+    LM head on rmsnorm(h0) (catches a dropped or doubled residual)."""
+    I = _fwd_inputs(14, 2, 5, 32, 2, 1, 16, 20, 6, 3, "f32")
+    for lw in I["layers"]:
+        lw["wo"] = np.zeros_like(lw["wo"])
+    par = [-1, 0, 0, 1, 2]
+    o = oracle.verify_forward(I["h0"], I["layers"], I["g_final"], I["w_lm"], I["k_caches"],
+                              I["v_caches"], [3, 6], par, 2, 1, 16, "f32")
+    z = oracle.verify_forward(I["h0"], [], I["g_final"], I["w_lm"], I["k_caches"], [], [3, 6],
+                              par, 2, 1, 16, "f32")
+    np.testing.assert_array_equal(o["hidden"], oracle.decode(I["h0"], "f32"))
+    np.testing.assert_allclose(o["logits"], z["logits"], rtol=1e-12)
+
+
+def test_forward_uniform_attention_by_hand():
+    """Wq = 0 makes every score 0, so a node's attention output is the mean
+    of the visible values: the L_b cached rows and its ancestors-or-self.
+    With Wv = I, the values of the tree are x itself; Wo is a permutation
+    (y[i] = o[pi(i)] in the [out][in] layout), which pins its orientation."""
+    d = dh = 16
+    rng = np.random.default_rng(15)
+    h0 = rng.standard_normal((1, 4, d)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    pi = np.roll(np.arange(d), 3)                       # not an involution
+    wo = np.zeros((d, d), np.float32)
+    wo[np.arange(d), pi] = 1.0
+    layer = {"g": g, "wq": np.zeros((d, d), np.float32), "wk": rng.standard_normal((d, d)).astype(np.float32),
+             "wv": np.eye(d, dtype=np.float32), "wo": wo}
+    L, Lcap = 3, 5
+    kc = rng.standard_normal((1, 1, Lcap, dh)).astype(np.float32)
+    vc = rng.standard_normal((1, 1, Lcap, dh)).astype(np.float32)
+    par = [-1, 0, 1, 0]
+    o = oracle.verify_forward(h0, [layer], np.ones(d, np.float32), np.eye(d, dtype=np.float32),
+                              [kc], [vc], [L], par, 1, 1, dh, "f32")
+    h = h0[0].astype(np.float64)
+    x = h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + 1e-6) * g
+    x = x.astype(np.float32).astype(np.float64)         # the fp32 rounding point
+    paths = {0: [0], 1: [0, 1], 2: [0, 1, 2], 3: [0, 3]}
+    for n in range(4):
+        att = (vc[0, 0, :L].astype(np.float64).sum(0) + x[paths[n]].sum(0)) / (L + len(paths[n]))
+        att = att.astype(np.float32).astype(np.float64)
+        np.testing.assert_allclose(o["hidden"][0, n], h[n] + att[pi], rtol=1e-12, atol=1e-12)
