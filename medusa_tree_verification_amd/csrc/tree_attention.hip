@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
     using C = Cfg<T, DH>;
     constexpr int NT = NW * kWave;
     __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
-    __shared__ uint8_t par[MEDUSA_MAX_TREE];
+    __shared__ __attribute__((aligned(16))) uint8_t par[MEDUSA_MAX_TREE];
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid % kWave, wave = tid / kWave;
@@ -284,7 +284,12 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
     const int b = (int)(lid / ((uint32_t)p.nmt * p.nsplit * p.Hkv));
 
     // The prefix length, this lane's query row and the parent table are
-    // loaded together, before the first wait.
+    // loaded together, before the first wait.  The parent table
+    // (kernel-argument bytes) is read into registers first and written to LDS
+    // after the query loads are issued: loads complete in order, so waiting
+    // for it then does not wait for them.
+    static_assert(MEDUSA_MAX_TREE % 4 == 0 && MEDUSA_MAX_TREE / 4 <= 4 * kWave, "parent words");
+    const uint32_t parw = tid < MEDUSA_MAX_TREE / 4 ? reinterpret_cast<const uint32_t *>(p.parent)[tid] : 0u;
     const int Lraw = p.prefix_len[b];
     const int col = lane & 31, h = lane >> 5;
     // with the key split, waves w and w + W share rows: wave group kgrp takes
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
         for (int ks = 0; ks < C::NKS; ++ks)
             qf[ks] = buf_ld16(qr, qoff + (uint32_t)(ks * C::KSTEP * sizeof(T)));
     }
-    for (int i = tid; i < p.T; i += nthr) par[i] = p.parent[i];
+    if (tid < MEDUSA_MAX_TREE / 4) reinterpret_cast<uint32_t *>(par)[tid] = parw;
 
     if (lid == 0 && tid == 0) {
         int bad = 0;
