@@ -43,7 +43,7 @@ namespace {
 constexpr int kGemmWaves = 4;       // waves per workgroup, each a slice of the WG's K range
 constexpr int kGemmTiles = 4;       // 16-row W tiles per workgroup
 constexpr int kGemmRows = 16 * kGemmTiles;
-constexpr int kGemmCols = 64;       // X rows per workgroup (MT <= 4 tiles of 16)
+constexpr int kGemmCols = 64;       // X rows per workgroup of the streaming kernel (MT <= 4 tiles of 16)
 constexpr int kGemmUnroll = 4;      // k-steps per batch of loads
 // Staged kernel (K a multiple of one stage, 32 < M): X through LDS.
 constexpr int kLdsWaves = 4;
@@ -219,16 +219,17 @@ template <typename T, int MT>
 struct LdsCfg {
     static constexpr int KC = Elem<T>::kPer16B;
     static constexpr int KSTEP = 4 * KC;
-    static constexpr int SK = kLdsU * KSTEP;                           // k per stage
-    static constexpr int CHUNKS = kLdsU * MT * kWave;                  // 16-B X chunks per stage
+    static constexpr int U = MT >= 8 ? kLdsU / 2 : kLdsU;              // k-steps per stage
+    static constexpr int SK = U * KSTEP;                               // k per stage
+    static constexpr int CHUNKS = U * MT * kWave;                      // 16-B X chunks per stage
     static constexpr int XPT = CHUNKS / (kLdsWaves * kWave);           // per thread
     static_assert(CHUNKS % (kLdsWaves * kWave) == 0, "X stage split");
 };
 
 // Issue one stage's loads: this thread's X chunks first (they are waited
 // for first, to be stored to LDS), then this wave's W tiles.
-template <typename T, int MT, int XPT>
-__device__ __forceinline__ void lds_load_stage(u32x4 (&w)[kLdsTW][kLdsU], u32x4 (&xr)[XPT],
+template <typename T, int MT, int U, int XPT>
+__device__ __forceinline__ void lds_load_stage(u32x4 (&w)[kLdsTW][U], u32x4 (&xr)[XPT],
                                                const T *const (&arow)[kLdsTW],
                                                const T *const (&xrow)[XPT], const int (&koff)[XPT],
                                                int k0, int xT, int xsh) {
@@ -236,17 +237,17 @@ __device__ __forceinline__ void lds_load_stage(u32x4 (&w)[kLdsTW][kLdsU], u32x4 
 #pragma unroll
     for (int i = 0; i < XPT; ++i) xr[i] = ld16(xrow[i] + x_off(k0 + koff[i], xT, xsh));
 #pragma unroll
-    for (int u = 0; u < kLdsU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < kLdsTW; ++r) w[r][u] = ld16(arow[r] + k0 + u * KSTEP);
 }
 
-template <typename T, int MT>
+template <typename T, int MT, int U>
 __device__ __forceinline__ void lds_compute_stage(f32x4 (&acc)[kLdsTW][MT],
-                                                  const u32x4 (&w)[kLdsTW][kLdsU],
+                                                  const u32x4 (&w)[kLdsTW][U],
                                                   const u32x4 *xs, int lane) {
 #pragma unroll
-    for (int u = 0; u < kLdsU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
             const u32x4 xb = xs[(u * MT + j) * kWave + lane];
@@ -257,7 +258,7 @@ __device__ __forceinline__ void lds_compute_stage(f32x4 (&acc)[kLdsTW][MT],
 
 // Staged kernel.  One workgroup: W rows [n0, n0 + 128) (32 per wave) x X
 // rows [m0, m0 + 16 MT) over the stages of split s.  X's stage (16 MT rows
-// x kLdsU k-steps) is loaded once per workgroup into LDS, already in the
+// x U k-steps: 4, or 2 with 128 rows) is loaded once per workgroup into LDS, already in the
 // MFMA operand order, and read by all four waves; the next stage's X and W
 // loads are issued before the current stage's MFMAs (two LDS buffers, two
 // register sets for W, one barrier per stage).
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(kLdsWaves *kWave, 2) void gemm_lds_kernel(GemmArgs 
     const int g = lane / 16, c = lane % 16;
     const int lid = (int)xcd_logical_id(blockIdx.x, gridDim.x);
     const int mg = lid % a.MG, s = (lid / a.MG) % a.S, rb = lid / (a.MG * a.S);
-    const int n0 = rb * kLdsRows + wave * kLdsTW * 16, m0 = mg * kGemmCols;
+    const int n0 = rb * kLdsRows + wave * kLdsTW * 16, m0 = mg * 16 * MT;
     const int M = a.M, N = a.N, K = a.K, xT = a.xT, xsh = a.xsh;
     // the segment of this wave's rows; a wave wholly past N (N not a
     // multiple of 32) reads row N - 1 of the last segment, never before it
@@ -305,8 +306,8 @@ __global__ __launch_bounds__(kLdsWaves *kWave, 2) void gemm_lds_kernel(GemmArgs 
         for (int j = 0; j < MT; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (sb < se) {
-        u32x4 wa[kLdsTW][kLdsU], wb[kLdsTW][kLdsU], xr[C::XPT];
-        lds_load_stage<T, MT, C::XPT>(wa, xr, arow, xrow, koff, sb * C::SK, xT, xsh);
+        u32x4 wa[kLdsTW][C::U], wb[kLdsTW][C::U], xr[C::XPT];
+        lds_load_stage<T, MT, C::U, C::XPT>(wa, xr, arow, xrow, koff, sb * C::SK, xT, xsh);
 #pragma unroll
         for (int i = 0; i < C::XPT; ++i) xs[0][tid + i * kLdsWaves * kWave] = xr[i];
         __syncthreads();
@@ -314,27 +315,27 @@ __global__ __launch_bounds__(kLdsWaves *kWave, 2) void gemm_lds_kernel(GemmArgs 
         // stages alternate between the W register sets wa and wb
         while (true) {
             if (st + 1 < se) {
-                lds_load_stage<T, MT, C::XPT>(wb, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
+                lds_load_stage<T, MT, C::U, C::XPT>(wb, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
                 __builtin_amdgcn_sched_barrier(0);
-                lds_compute_stage<T, MT>(acc, wa, xs[buf], lane);
+                lds_compute_stage<T, MT, C::U>(acc, wa, xs[buf], lane);
 #pragma unroll
                 for (int i = 0; i < C::XPT; ++i) xs[buf ^ 1][tid + i * kLdsWaves * kWave] = xr[i];
                 __syncthreads();
             } else {
-                lds_compute_stage<T, MT>(acc, wa, xs[buf], lane);
+                lds_compute_stage<T, MT, C::U>(acc, wa, xs[buf], lane);
                 break;
             }
             ++st;
             buf ^= 1;
             if (st + 1 < se) {
-                lds_load_stage<T, MT, C::XPT>(wa, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
+                lds_load_stage<T, MT, C::U, C::XPT>(wa, xr, arow, xrow, koff, (st + 1) * C::SK, xT, xsh);
                 __builtin_amdgcn_sched_barrier(0);
-                lds_compute_stage<T, MT>(acc, wb, xs[buf], lane);
+                lds_compute_stage<T, MT, C::U>(acc, wb, xs[buf], lane);
 #pragma unroll
                 for (int i = 0; i < C::XPT; ++i) xs[buf ^ 1][tid + i * kLdsWaves * kWave] = xr[i];
                 __syncthreads();
             } else {
-                lds_compute_stage<T, MT>(acc, wb, xs[buf], lane);
+                lds_compute_stage<T, MT, C::U>(acc, wb, xs[buf], lane);
                 break;
             }
             ++st;
@@ -545,16 +546,20 @@ struct GemmPlan {
 // need_part forces partials (an epilogue reads them).
 inline GemmPlan gemm_plan(int M, int N, int K, int kstep, bool need_part) {
     GemmPlan g;
-    g.MG = (M + kGemmCols - 1) / kGemmCols;
-    g.MT = M >= kGemmCols ? 4 : (M + 15) / 16;
     const int KS = K / kstep;
-    g.staged = g.MT >= 2 && KS % kLdsU == 0;
+    const int mt = M >= kGemmCols ? 4 : (M + 15) / 16;
+    g.staged = mt >= 2 && KS % kLdsU == 0;
+    // staged with more than 64 rows: 128 X rows per workgroup (W read from
+    // L2 once per 128 rows instead of per 64)
+    g.MT = g.staged && M > kGemmCols ? 8 : mt;
+    const int cols = g.staged ? 16 * g.MT : kGemmCols;
+    g.MG = (M + cols - 1) / cols;
     int smax, S;
     if (g.staged) {
         g.RB = (N + kLdsRows - 1) / kLdsRows;
         const int units = g.RB * g.MG;
         S = units >= 3 * kNumCU / 4 ? 1 : (2 * kNumCU + units / 2) / units;
-        smax = KS / kLdsU / 4;
+        smax = KS / (g.MT >= 8 ? kLdsU / 2 : kLdsU) / 4;
     } else {
         g.RB = (N + kGemmRows - 1) / kGemmRows;
         const int units = g.RB * g.MG;
@@ -615,7 +620,7 @@ void launch_gemm_kernel(const GemmPlan &g, const GemmArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((gemm_lds_kernel<T, MT < 2 ? 2 : MT>), dim3((unsigned)(g.RB * g.S * g.MG)),
                            dim3(kLdsWaves * kWave), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_xwt_kernel<T, MT>), dim3((unsigned)(g.RB * g.S * g.MG)),
+        hipLaunchKernelGGL((gemm_xwt_kernel<T, MT < 4 ? MT : 4>), dim3((unsigned)(g.RB * g.S * g.MG)),
                            dim3(kGemmWaves * kWave), 0, st, a);
 }
 
@@ -640,7 +645,8 @@ int run_gemm(const GemmPlan &g, GemmArgs a, float *Y, float *part, int accumulat
         case 1: launch_gemm_kernel<T, 1>(g, a, st); break;
         case 2: launch_gemm_kernel<T, 2>(g, a, st); break;
         case 3: launch_gemm_kernel<T, 3>(g, a, st); break;
-        default: launch_gemm_kernel<T, 4>(g, a, st); break;
+        case 4: launch_gemm_kernel<T, 4>(g, a, st); break;
+        default: launch_gemm_kernel<T, 8>(g, a, st); break;
     }
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (!a.direct && epi_sum) {
