@@ -382,29 +382,6 @@ __global__ __launch_bounds__(kEpiThreads) void epi_sum_kernel(const float *__res
     }
 }
 
-struct RopeTab {
-    const int32_t *prefix_len;
-    double2 *tab;               // [B][T][dh/2]: cos, sin of the rotary angle
-    int B, T, dh, Lcap;
-    double theta;
-    uint8_t depth[MEDUSA_MAX_TREE];
-};
-
-// cos and sin of pos * theta^(-2j/dh) at pos = clamp(L_b, 0, Lcap) + depth(t),
-// in fp64; the same for every block.
-__global__ __launch_bounds__(kEpiThreads) void rope_table_kernel(RopeTab p) {
-    const int half = p.dh / 2, total = p.B * p.T * half;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
-        const int j = i % half, t = (i / half) % p.T, b = i / (half * p.T);
-        int L = p.prefix_len[b];
-        L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
-        const double ang = (double)(L + p.depth[t]) * pow(p.theta, -2.0 * j / p.dh);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        p.tab[i] = make_double2(cs, sn);
-    }
-}
-
 struct QkvEpi {
     const float *part;          // [S][M][N], N = (Hq + 2 Hkv) dh: q | k | v columns
     const double2 *tab;         // rotary table [M][dh/2]
@@ -478,43 +455,81 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 v) {
 
 constexpr int kNormU = 4;   // groups of 4 elements per thread per pass step
 
+struct NormArgs {
+    const void *in;             // FROM_IN: the first block's input rows [M][d] (dtype)
+    float *h;                   // fp32 residual stream [M][d]
+    const float *part;          // NS > 0: output-projection partials [NS][M][d]
+    size_t md;                  // M * d
+    const void *gain;           // [d] dtype
+    void *x;                    // normalised rows [M][d] (dtype)
+    int d;
+    float eps;
+    // rotary table, written when tab != nullptr: row m's dh/2 (cos, sin)
+    double2 *tab;
+    const int32_t *prefix_len;
+    int T, dh, Lcap;
+    double theta;
+    uint8_t depth[MEDUSA_MAX_TREE];
+};
+
 // x[m] = rmsnorm(h[m]) g rounded to the dtype, one workgroup per row, four
-// elements per thread access with kNormU accesses in flight.  With FROM_IN
-// the row is read from the dtype input (the first block) and also stored to
-// h as fp32, which starts the residual stream.  Every thread reads back only
-// what it wrote itself.
-template <typename T, bool FROM_IN>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const T *__restrict__ in,
-                                                               float *__restrict__ h,
-                                                               const T *__restrict__ gain,
-                                                               T *__restrict__ x, int d, float eps) {
+// elements per thread access with kNormU accesses in flight.  The residual
+// update comes first: with FROM_IN the row is read from the dtype input (the
+// first block) and starts the fp32 residual stream; with NS > 0 the previous
+// block's output-projection partials are summed (in split order) and added
+// to h.  h is stored back in both cases; every thread reads back only what
+// it wrote itself.  The first block's launch also writes row m of the
+// rotary table: cos and sin of pos * theta^(-2j/dh) at
+// pos = clamp(L_b, 0, Lcap) + depth(t), in fp64 (the same for every block).
+template <typename T, bool FROM_IN, int NS>
+__global__ __launch_bounds__(kNormThreads) void norm_kernel(NormArgs a) {
     __shared__ float red[kNormThreads / kWave];
-    const size_t row = (size_t)blockIdx.x * d;
-    const int d4 = d / 4;
+    const int m = blockIdx.x;
+    if (a.tab && (int)threadIdx.x < a.dh / 2) {
+        const int j = threadIdx.x, b = m / a.T, t = m - b * a.T;
+        int L = a.prefix_len[b];
+        L = L < 0 ? 0 : (L > a.Lcap ? a.Lcap : L);
+        const double ang = (double)(L + a.depth[t]) * pow(a.theta, -2.0 * j / a.dh);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        a.tab[(size_t)m * (a.dh / 2) + j] = make_double2(cs, sn);
+    }
+    const size_t row = (size_t)m * a.d;
+    const int d4 = a.d / 4;
+    float *h = a.h;
     float ss = 0.f;
     for (int b = 0; b < d4; b += kNormU * kNormThreads) {
-        f32x4 v[kNormU];
+        f32x4 v[kNormU], pv[kNormU][NS > 0 ? NS : 1];
 #pragma unroll
         for (int u = 0; u < kNormU; ++u) {
             const int c4 = b + u * kNormThreads + threadIdx.x;
-            v[u] = c4 < d4 ? (FROM_IN ? load4<T>(in + row + 4 * c4) : load4<float>(h + row + 4 * c4))
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int cc = c4 < d4 ? c4 : d4 - 1;
+            v[u] = FROM_IN ? load4<T>((const T *)a.in + row + 4 * cc) : load4<float>(h + row + 4 * cc);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) pv[u][s] = load4<float>(a.part + s * a.md + row + 4 * cc);
         }
 #pragma unroll
         for (int u = 0; u < kNormU; ++u) {
             const int c4 = b + u * kNormThreads + threadIdx.x;
-            if (FROM_IN && c4 < d4) store4<float>(h + row + 4 * c4, v[u]);
+            if (c4 >= d4) continue;
+            if (NS > 0) {
+                f32x4 t = pv[u][0];
+#pragma unroll
+                for (int s = 1; s < NS; ++s) t += pv[u][s];
+                v[u] += t;
+            }
+            if (FROM_IN || NS > 0) store4<float>(h + row + 4 * c4, v[u]);
             ss += v[u][0] * v[u][0] + v[u][1] * v[u][1] + v[u][2] * v[u][2] + v[u][3] * v[u][3];
         }
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    for (int mm = 32; mm >= 1; mm >>= 1) ss += __shfl_xor(ss, mm);
     if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
-    const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+    const float inv = 1.0f / sqrtf(tot / (float)a.d + a.eps);
     for (int b = 0; b < d4; b += kNormU * kNormThreads) {
         f32x4 v[kNormU], gv[kNormU];
 #pragma unroll
@@ -522,12 +537,12 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const T *__restri
             const int c4 = b + u * kNormThreads + threadIdx.x;
             const int cc = c4 < d4 ? c4 : d4 - 1;
             v[u] = load4<float>(h + row + 4 * cc);
-            gv[u] = load4<T>(gain + 4 * cc);
+            gv[u] = load4<T>((const T *)a.gain + 4 * cc);
         }
 #pragma unroll
         for (int u = 0; u < kNormU; ++u) {
             const int c4 = b + u * kNormThreads + threadIdx.x;
-            if (c4 < d4) store4<T>(x + row + 4 * c4, v[u] * inv * gv[u]);
+            if (c4 < d4) store4<T>((T *)a.x + row + 4 * c4, v[u] * inv * gv[u]);
         }
     }
 }
@@ -730,30 +745,45 @@ int run_forward(const FwdArgs &f, char *ws, hipStream_t st) {
     const size_t kv_block = (size_t)M * f.Hkv * dh;   // one block's tree keys (or values)
     const int xsh = dh == 128 ? 7 : 6;
 
-    if (f.N > 0) {
-        RopeTab rt;
-        rt.prefix_len = f.prefix_len;
-        rt.tab = (double2 *)(ws + L.tab);
-        rt.B = f.B;
-        rt.T = f.T;
-        rt.dh = dh;
-        rt.Lcap = f.Lcap;
-        rt.theta = f.theta;
-        for (int i = 0; i < MEDUSA_MAX_TREE; ++i) rt.depth[i] = 0;
-        for (int n = 1; n < f.T; ++n) rt.depth[n] = (uint8_t)(rt.depth[f.parent[n]] + 1);
-        hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)M * dh / 2, kEpiThreads)),
-                           dim3(kEpiThreads), 0, st, rt);
-        if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
-    }
+    NormArgs na;
+    na.in = f.h0;
+    na.h = h;
+    na.part = part;
+    na.md = (size_t)M * f.d;
+    na.x = x;
+    na.d = f.d;
+    na.eps = f.eps;
+    na.tab = nullptr;
+    na.prefix_len = f.prefix_len;
+    na.T = f.T;
+    na.dh = dh;
+    na.Lcap = f.Lcap;
+    na.theta = f.theta;
+    for (int i = 0; i < MEDUSA_MAX_TREE; ++i) na.depth[i] = 0;
+    for (int n = 1; n < f.T; ++n) na.depth[n] = (uint8_t)(na.depth[f.parent[n]] + 1);
+    // the output projection's partials (when it splits K) are added to h by
+    // the next norm
+    const int wo_ns = L.wo.part_bytes ? L.wo.S : 0;
 
     for (int l = 0; l <= f.N; ++l) {
-        const T *gain = (const T *)(l < f.N ? f.g[l] : f.g_final);
-        if (l == 0)
-            hipLaunchKernelGGL((rmsnorm_kernel<T, true>), dim3(M), dim3(kNormThreads), 0, st,
-                               (const T *)f.h0, h, gain, x, f.d, f.eps);
-        else
-            hipLaunchKernelGGL((rmsnorm_kernel<T, false>), dim3(M), dim3(kNormThreads), 0, st,
-                               (const T *)nullptr, h, gain, x, f.d, f.eps);
+        na.gain = l < f.N ? f.g[l] : f.g_final;
+        na.tab = l == 0 && f.N > 0 ? (double2 *)(ws + L.tab) : nullptr;
+        const dim3 ng((unsigned)M), nb(kNormThreads);
+        if (l == 0) {
+            hipLaunchKernelGGL((norm_kernel<T, true, 0>), ng, nb, 0, st, na);
+        } else {
+            switch (wo_ns) {
+                case 0: hipLaunchKernelGGL((norm_kernel<T, false, 0>), ng, nb, 0, st, na); break;
+                case 1: hipLaunchKernelGGL((norm_kernel<T, false, 1>), ng, nb, 0, st, na); break;
+                case 2: hipLaunchKernelGGL((norm_kernel<T, false, 2>), ng, nb, 0, st, na); break;
+                case 3: hipLaunchKernelGGL((norm_kernel<T, false, 3>), ng, nb, 0, st, na); break;
+                case 4: hipLaunchKernelGGL((norm_kernel<T, false, 4>), ng, nb, 0, st, na); break;
+                case 5: hipLaunchKernelGGL((norm_kernel<T, false, 5>), ng, nb, 0, st, na); break;
+                case 6: hipLaunchKernelGGL((norm_kernel<T, false, 6>), ng, nb, 0, st, na); break;
+                case 7: hipLaunchKernelGGL((norm_kernel<T, false, 7>), ng, nb, 0, st, na); break;
+                default: hipLaunchKernelGGL((norm_kernel<T, false, 8>), ng, nb, 0, st, na); break;
+            }
+        }
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
         if (l == f.N) break;
 
@@ -778,7 +808,7 @@ int run_forward(const FwdArgs &f, char *ws, hipStream_t st) {
         GemmArgs oa = gemm_args(att, f.wo[l], M, f.d, f.Hq * dh);
         oa.xT = f.T;
         oa.xsh = xsh;
-        if ((rc = run_gemm<T>(L.wo, oa, h, part, 1, true, st)) != MEDUSA_OK) return rc;
+        if ((rc = run_gemm<T>(L.wo, oa, h, part, 1, false, st)) != MEDUSA_OK) return rc;
     }
     return run_gemm<T>(L.lm, gemm_args(x, f.w_lm, M, f.V, f.d), f.logits, part, 0, true, st);
 }
