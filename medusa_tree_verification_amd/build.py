@@ -26,7 +26,10 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=1800)
+    except subprocess.TimeoutExpired as e:
+        raise RuntimeError(f"hipcc did not finish within {e.timeout} s") from None
     # the host pass does not know the packed-fp32 feature name; that note is harmless
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
