@@ -52,13 +52,14 @@ def algorithmic_bytes(wl, prefix_len, n_internal):
     w = 2 if wl.dtype == W.BF16 else 4
     B, K, d, V, s, T = wl.B, wl.K, wl.d, wl.V, wl.s, wl.T
     stage1 = K * d * d * w + B * d * w + B * K * d * w              # W1, h in; z out
-    stage2 = K * V * d * w + B * K * d * w + B * K * s * 8          # W2, z in; ids+vals out
+    stage2 = K * V * d * w + B * K * d * w                          # W2, z in (stream kernel)
+    merge = B * K * s * 8                                           # ids + vals out
     Ltot = int(np.minimum(prefix_len, wl.Lcap).sum())
     attn = (2 * wl.Hkv * Ltot * wl.dh * w + 2 * B * wl.Hkv * T * wl.dh * w
             + 2 * B * wl.Hq * T * wl.dh * w)                         # KV prefix + tree KV + q in, out
     accept = B * (n_internal + 1) * V * w                            # internal rows + best row
-    return {"heads_stage1": stage1, "heads_stage2": stage2, "tree_attention": attn,
-            "tree_accept": accept}
+    return {"heads_stage1": stage1, "heads_stage2": stage2, "heads_merge": merge,
+            "tree_attention": attn, "tree_accept": accept}
 
 
 def attention_flops(wl, prefix_len, tree):
@@ -173,16 +174,20 @@ def main():
         mv.medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws_h)
         if ev is not None:
             ev[1].record()
-        mv.medusa_heads_stage2(w2, B, K, d, V, s, ids, ws_h, topk_vals=vals)
+        # stage 2 as its two kernels, so that the weight stream can be timed alone
+        mv.medusa_heads_stage2_stream(w2, B, K, d, V, s, ws_h)
         if ev is not None:
             ev[2].record()
-        mv.tree_attention(q, kc, vc, plen, kt, vt, tree.parent, wl.scale, ws=ws_a, out=attn_out)
+        mv.medusa_heads_stage2_merge(B, K, d, V, s, dt, ids, ws_h, topk_vals=vals)
         if ev is not None:
             ev[3].record()
+        mv.tree_attention(q, kc, vc, plen, kt, vt, tree.parent, wl.scale, ws=ws_a, out=attn_out)
+        if ev is not None:
+            ev[4].record()
         mv.tree_accept(vlog, ids, tree.parent, mode, wl.temperature, wl.eps, wl.delta, ws=ws_c,
                        out=acc)
         if ev is not None:
-            ev[4].record()
+            ev[5].record()
 
     for _ in range(args.warmup):
         step()
@@ -199,11 +204,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    names = ["heads_stage1", "heads_stage2", "tree_attention", "tree_accept"]
+    names = ["heads_stage1", "heads_stage2", "heads_merge", "tree_attention", "tree_accept"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in
            enumerate(names)}
 
@@ -237,7 +242,7 @@ def main():
                                                      int(ax["prefix_len"].max())],
                    "acceptance": wl.mode, "parallelism": "single GPU"},
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"kernel": "medusa_heads_stage2: heads_stage2_kernel + heads_merge_kernel (W2 stream + top-s)", "bound": "hbm",
+        "roofline": {"kernel": "heads_stage2_kernel (medusa_heads_stage2_stream: W2 stream + fused per-workgroup top-s)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "stages": stages,

@@ -112,6 +112,17 @@ int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, int s, int d
                         float *logits_out, int32_t *topk_ids, float *topk_vals, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* The two kernels of medusa_heads_stage2 as separate calls (same arguments
+ * and workspace): the W2 stream with a top-s list per (workgroup, head,
+ * sequence) left in the workspace, then the merge of those lists into
+ * topk_ids / topk_vals.  medusa_heads_stage2 is exactly stream followed by
+ * merge on the same stream and workspace; the split lets a caller time the
+ * weight stream by itself. */
+int medusa_heads_stage2_stream(const void *w2, int B, int K, int d, int V, int s, int dtype,
+                               float *logits_out, void *ws, size_t ws_bytes, void *stream);
+int medusa_heads_stage2_merge(int B, int K, int d, int V, int s, int dtype, int32_t *topk_ids,
+                              float *topk_vals, void *ws, size_t ws_bytes, void *stream);
+
 size_t medusa_heads_topk_workspace_bytes(int B, int K, int d, int V, int s, int dtype);
 
 /* medusa_heads_topk plus the tree's root token: the base model's own next

@@ -26,7 +26,7 @@ STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "ME
           -7: "MEDUSA_ERR_LAUNCH"}
 
 EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
-           "medusa_heads_stage2",
+           "medusa_heads_stage2", "medusa_heads_stage2_stream", "medusa_heads_stage2_merge",
            "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
            "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
            "medusa_verify_forward", "medusa_verify_forward_workspace_bytes", "medusa_status_str",
@@ -49,6 +49,8 @@ def _load() -> ctypes.CDLL:
     L.medusa_heads_topk_root.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, Z, P]
     L.medusa_heads_stage1.argtypes = [P, P, I, I, I, I, I, I, P, Z, P]
     L.medusa_heads_stage2.argtypes = [P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    L.medusa_heads_stage2_stream.argtypes = [P, I, I, I, I, I, I, P, P, Z, P]
+    L.medusa_heads_stage2_merge.argtypes = [I, I, I, I, I, I, P, P, P, Z, P]
     L.medusa_heads_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.medusa_heads_topk_workspace_bytes.restype = Z
     L.tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, Z, P]
@@ -68,7 +70,8 @@ def _load() -> ctypes.CDLL:
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
     for f in ("medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
-              "medusa_heads_stage2", "tree_attention",
+              "medusa_heads_stage2", "medusa_heads_stage2_stream", "medusa_heads_stage2_merge",
+              "tree_attention",
               "tree_accept", "tree_commit_kv", "medusa_sample_token", "medusa_verify_forward"):
         getattr(L, f).restype = I
     return L
@@ -158,6 +161,19 @@ def medusa_heads_stage2(w2, B, K, d, V, s, topk_ids, ws, topk_vals=None, logits=
                                  _ptr(topk_ids), _ptr(topk_vals), _ptr(ws), ws.numel(),
                                  _stream(stream))
     _check("medusa_heads_stage2", rc)
+
+
+def medusa_heads_stage2_stream(w2, B, K, d, V, s, ws, logits=None, stream=None) -> None:
+    rc = lib.medusa_heads_stage2_stream(_ptr(w2), B, K, d, V, s, _dtype_code(w2), _ptr(logits),
+                                        _ptr(ws), ws.numel(), _stream(stream))
+    _check("medusa_heads_stage2_stream", rc)
+
+
+def medusa_heads_stage2_merge(B, K, d, V, s, dtype_code, topk_ids, ws, topk_vals=None,
+                              stream=None) -> None:
+    rc = lib.medusa_heads_stage2_merge(B, K, d, V, s, int(dtype_code), _ptr(topk_ids),
+                                       _ptr(topk_vals), _ptr(ws), ws.numel(), _stream(stream))
+    _check("medusa_heads_stage2_merge", rc)
 
 
 def tree_attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, parent, scale: float, *,

@@ -506,12 +506,12 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
-// w_lm == NULL: the K Medusa heads only; otherwise the LM head (input: the
-// hidden state) is streamed as head K and its argmax goes to root_token.
-int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, int K, int d,
-                  int V, int s, int dtype, float *logits_out, int32_t *topk_ids,
-                  float *topk_vals, int32_t *root_token, float *root_val, void *ws,
-                  hipStream_t st) {
+// The W2 stream with the fused per-workgroup top-s (partials into the
+// workspace).  w_lm == NULL: the K Medusa heads only; otherwise the LM head
+// (input: the hidden state) is streamed as head K.
+int launch_stage2_stream(const void *w2, const void *w_lm, const void *hidden, int B, int K,
+                         int d, int V, int s, int dtype, float *logits_out, void *ws,
+                         hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype, w_lm != nullptr);
     char *base = (char *)ws;
     float2 *part = (float2 *)(base + L.part_off);
@@ -530,12 +530,31 @@ int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, i
                            (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
                            L.P);
     }
-    if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
-    hipLaunchKernelGGL(heads_merge_kernel,
-                       dim3((unsigned)L.nh, (unsigned)((B + kS2Waves - 1) / kS2Waves)), block, 0,
-                       st, part, topk_ids,
-                       topk_vals, root_token, root_val, B, K, s, L.ntph, L.nt, L.P);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+// The merge of the partial lists into topk_ids / topk_vals (and, with the LM
+// head, root_token / root_val).
+int launch_stage2_merge(bool lm, int B, int K, int d, int V, int s, int dtype, int32_t *topk_ids,
+                        float *topk_vals, int32_t *root_token, float *root_val, void *ws,
+                        hipStream_t st) {
+    const HeadsLayout L = heads_layout(B, K, d, V, dtype, lm);
+    const float2 *part = (const float2 *)((char *)ws + L.part_off);
+    hipLaunchKernelGGL(heads_merge_kernel,
+                       dim3((unsigned)L.nh, (unsigned)((B + kS2Waves - 1) / kS2Waves)),
+                       dim3(kS2Waves * kWave), 0, st, part, topk_ids, topk_vals, root_token,
+                       root_val, B, K, s, L.ntph, L.nt, L.P);
+    return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+int launch_stage2(const void *w2, const void *w_lm, const void *hidden, int B, int K, int d,
+                  int V, int s, int dtype, float *logits_out, int32_t *topk_ids,
+                  float *topk_vals, int32_t *root_token, float *root_val, void *ws,
+                  hipStream_t st) {
+    const int rc = launch_stage2_stream(w2, w_lm, hidden, B, K, d, V, s, dtype, logits_out, ws, st);
+    if (rc != MEDUSA_OK) return rc;
+    return launch_stage2_merge(w_lm != nullptr, B, K, d, V, s, dtype, topk_ids, topk_vals,
+                               root_token, root_val, ws, st);
 }
 
 }  // namespace
@@ -568,6 +587,29 @@ extern "C" int medusa_heads_stage2(const void *w2, int B, int K, int d, int V, i
     if (st != MEDUSA_OK) return st;
     return launch_stage2(w2, nullptr, nullptr, B, K, d, V, s, dtype, logits_out, topk_ids,
                          topk_vals, nullptr, nullptr, ws, (hipStream_t)stream);
+}
+
+extern "C" int medusa_heads_stage2_stream(const void *w2, int B, int K, int d, int V, int s,
+                                          int dtype, float *logits_out, void *ws, size_t ws_bytes,
+                                          void *stream) {
+    int st = check_heads_args(w2, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2_stream(w2, nullptr, nullptr, B, K, d, V, s, dtype, logits_out, ws,
+                                (hipStream_t)stream);
+}
+
+extern "C" int medusa_heads_stage2_merge(int B, int K, int d, int V, int s, int dtype,
+                                         int32_t *topk_ids, float *topk_vals, void *ws,
+                                         size_t ws_bytes, void *stream) {
+    int st = check_heads_args((const void *)1, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!topk_ids) return MEDUSA_ERR_NULL;
+    st = check_ws(ws, ws_bytes, heads_layout(B, K, d, V, dtype).total);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2_merge(false, B, K, d, V, s, dtype, topk_ids, topk_vals, nullptr, nullptr,
+                               ws, (hipStream_t)stream);
 }
 
 extern "C" int medusa_heads_topk(const void *hidden, const void *w1, const void *w2, int B, int K,

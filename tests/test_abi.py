@@ -179,3 +179,14 @@ def test_forward_validation(mv):
     ws = L.medusa_verify_forward_workspace_bytes(1, 4, 256, 4, 2, 64, 128, 1000, 1)
     assert ws >= 4 * 256 * 4                     # the fp32 residual stream at least
     assert L.medusa_verify_forward_workspace_bytes(1, 4, 100, 4, 2, 64, 128, 1000, 1) == 0
+
+
+def test_stage2_split_validation(mv):
+    L = mv.lib
+    assert L.medusa_heads_stage2_stream(None, 1, 4, 4096, 32000, 3, 1, None, FAKE_WS, 1 << 40, None) == -1
+    assert L.medusa_heads_stage2_stream(FAKE, 17, 4, 4096, 32000, 3, 1, None, FAKE_WS, 1 << 40, None) == -2
+    assert L.medusa_heads_stage2_stream(FAKE, 1, 4, 4096, 32000, 3, 1, None, FAKE_WS, 64, None) == -5
+    assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 3, 1, None, None, FAKE_WS, 1 << 40, None) == -1
+    assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 9, 1, FAKE, None, FAKE_WS, 1 << 40, None) == -2
+    assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 3, 7, FAKE, None, FAKE_WS, 1 << 40, None) == -3
+    assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 3, 1, FAKE, None, None, 1 << 40, None) == -5

@@ -94,6 +94,14 @@ def test_heads_stages_equal_fused_call_and_repeat_bit_identical():
         torch.cuda.synchronize()
         assert torch.equal(ids, a["topk_ids"]) and torch.equal(vals, a["topk_vals"])
         assert torch.equal(lg, a["logits"])
+    # the stream and the merge as separate calls give the same bits
+    ids.fill_(-1)
+    vals.zero_()
+    mv.medusa_heads_stage1(h, w1, B, K, d, V, s, ws)
+    mv.medusa_heads_stage2_stream(w2, B, K, d, V, s, ws)
+    mv.medusa_heads_stage2_merge(B, K, d, V, s, mv.BF16, ids, ws, topk_vals=vals)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, a["topk_ids"]) and torch.equal(vals, a["topk_vals"])
     del wl
 
 
