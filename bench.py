@@ -174,12 +174,14 @@ def main():
         mv.medusa_heads_stage1(hidden, w1, B, K, d, V, s, ws_h)
         if ev is not None:
             ev[1].record()
-        # stage 2 as its two kernels, so that the weight stream can be timed alone
-        mv.medusa_heads_stage2_stream(w2, B, K, d, V, s, ws_h)
-        if ev is not None:
+        if ev is None:
+            mv.medusa_heads_stage2(w2, B, K, d, V, s, ids, ws_h, topk_vals=vals)
+        else:
+            # the same two kernels as two calls, so that the weight stream is
+            # timed alone
+            mv.medusa_heads_stage2_stream(w2, B, K, d, V, s, ws_h)
             ev[2].record()
-        mv.medusa_heads_stage2_merge(B, K, d, V, s, dt, ids, ws_h, topk_vals=vals)
-        if ev is not None:
+            mv.medusa_heads_stage2_merge(B, K, d, V, s, dt, ids, ws_h, topk_vals=vals)
             ev[3].record()
         mv.tree_attention(q, kc, vc, plen, kt, vt, tree.parent, wl.scale, ws=ws_a, out=attn_out)
         if ev is not None:

@@ -151,3 +151,14 @@ def test_forward_gqa_batch_shape():
     t = W.workload_tree(wl)
     I = W.forward_inputs(wl, 1)
     _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
+
+
+def test_forward_max_tree():
+    """T = 256 (the largest tree), B = 2: 512 rows in 128-row column groups,
+    positions up to L_b + depth 5, a tree from the five-head pruning."""
+    wl = _wl("large_vocab_typical", cid=35, B=2, d=256, V=999, Hq=4, Hkv=2, dh=64, L_lo=40,
+             L_hi=90)
+    t = W.workload_tree(dataclasses.replace(wl, d=4096))   # the 256-node tree
+    assert t.T == 256
+    I = W.forward_inputs(wl, 2, T=t.T)
+    _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
