@@ -2,9 +2,10 @@
 """Throughput of the Medusa verify step on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the K Medusa heads
-with top-s (two launches: W1 stage, W2 stage with fused top-s), one tree
-attention pass over the KV prefix and the tree, and tree acceptance.  Inputs
-are seeded synthetic tensors resident in HBM before timing starts.
+with top-s (W1 stage; W2 stream with a fused per-workgroup top-s; merge of
+those lists), one tree attention pass over the KV prefix and the tree, and
+tree acceptance.  Inputs are seeded synthetic tensors resident in HBM before
+timing starts.
 
 Prints one JSON line.  Per-call durations come from HIP events recorded on
 the stream the library launches on (torch's current stream).
@@ -27,6 +28,7 @@ from medusa_tree_verification_amd import workloads as W  # noqa: E402
 
 METRIC = "tree-verify steps/s (heads+tree-attn+accept); achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 
 
@@ -221,6 +223,16 @@ def main():
                   "GBps": round(nbytes[n] / (per[n] * 1e-3) / 1e9, 1)} for n in names}
     stages["tree_attention"]["TFLOPs"] = round(flops / (per["tree_attention"] * 1e-3) / 1e12, 1)
     step_bytes = sum(nbytes.values())
+    # roofline time of every stage (HBM at the published peak; the tree
+    # attention at max(HBM, bf16 MFMA peak) since long prefixes are
+    # MFMA-bound) and each stage's and the step's fraction of it
+    roof_us = {n: nbytes[n] / (PEAK_HBM_GBS * 1e9) * 1e6 for n in names}
+    roof_us["tree_attention"] = max(roof_us["tree_attention"], flops / (PEAK_MFMA_TFLOPS * 1e12) * 1e6)
+    for n in names:
+        stages[n]["roofline_frac"] = round(roof_us[n] / (per[n] * 1e3), 4)
+    stages["tree_attention"]["bound"] = ("mfma" if flops / (PEAK_MFMA_TFLOPS * 1e12) >
+                                         nbytes["tree_attention"] / (PEAK_HBM_GBS * 1e9) else "hbm")
+    step_us = np.array([e[0].elapsed_time(e[5]) for e in evs]) * 1e3
 
     dom = "heads_stage2"
     achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
@@ -244,6 +256,9 @@ def main():
                                                      int(ax["prefix_len"].max())],
                    "acceptance": wl.mode, "parallelism": "single GPU"},
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_roofline_frac": round(sum(roof_us.values()) / (ms_per_step * 1e3), 4),
+        "step_us_p50_p90": [round(float(np.percentile(step_us, 50)), 2),
+                            round(float(np.percentile(step_us, 90)), 2)],
         "roofline": {"kernel": "heads_stage2_kernel (medusa_heads_stage2_stream: W2 stream + fused per-workgroup top-s)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
