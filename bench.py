@@ -107,9 +107,9 @@ def calibrate_copy(mib, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the verify step shards by sequence, kv head or vocabulary; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (the verify step "
+              "would shard by sequence, kv head or vocabulary). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if args.calibrate_copy_mib:

@@ -16,7 +16,7 @@
  * 5.3 verification that stops at the first mismatch) and the aiunderstanding
  * page (accept the longest matching prefix).
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - weights are [out][in] (torch Linear); no biases.
  *  - bf16 mode: one rounding point, z = SiLU(W1 h) + h is rounded to bf16
  *    (nearest-even) from its fp32 value before W2; logits are not rounded.
