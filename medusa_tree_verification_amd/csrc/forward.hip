@@ -17,8 +17,10 @@
 // A operand of 16x16 MFMA tiles and X, small and L2-resident, is the B
 // operand.  With M > 16, X is staged through LDS once per workgroup of 128
 // W rows and shared by its four waves, so that X costs few load
-// instructions per W byte (the load path, not HBM, limits otherwise).  S
-// workgroups per row block may split K; they leave fp32 partials that an
+// instructions per W byte (the load path, not HBM, limits otherwise).  With
+// more than 256 rows (bf16) the products dominate: 256 x 256 output tiles
+// with both operands brought into LDS by direct loads of whole cache lines
+// (the large kernel).  S workgroups per tile may split K; they leave fp32 partials that an
 // epilogue kernel sums in a fixed order, so results do not depend on
 // timing.  The q/k/v epilogue also applies the rotary embedding (from a
 // per-call fp64 table of cos/sin at every node's position) and writes the
@@ -349,6 +351,171 @@ __global__ __launch_bounds__(kLdsWaves *kWave, 2) void gemm_lds_kernel(GemmArgs 
             gemm_store(a, s, m0 + 16 * j + c, n0 + 16 * r + 4 * g, acc[r][j]);
 }
 
+// ---- large kernel (bf16, many rows): both operands through LDS
+// One workgroup: W rows [n0, n0 + 256) x X rows [m0, m0 + 256) over the
+// 64-k stages of split s.  Each stage of both operands is brought into LDS
+// by direct global-to-LDS loads: one load instruction moves 8 rows x 128 B
+// (8 lanes per row, whole cache lines), lane l landing at slot l of a
+// kilobyte.  Row r of a 16-row tile keeps its 16-B chunk c at slot
+// c ^ ((r >> 1) & 7), so that the MFMA fragment reads (row l % 16, chunk
+// l / 16 of a k-step) hit 16 distinct slots per 16 lanes.  Wave w computes
+// W tiles 8 (w & 1) .. + 7 against X tiles 8 (w >> 1) .. + 7 (64 products
+// of 16 x 16 per k-step).  Two stage buffers: the loads of stage st + 2 go
+// into stage st's buffer once every wave has read stage st (one barrier per
+// stage), spread over the first quarter of the following products; the
+// fragments of the next k-step are read while the current one's products
+// run.  The load counter is waited on by hand (all loads of this wave are
+// the stage loads), since a full barrier with fences would drain the loads
+// in flight.
+constexpr int kBigTile = 256;
+constexpr int kBigMinRows = 256;
+constexpr int kBigSK = 64;          // k per stage (two k-steps of 32)
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) const void *gbl_ptr_t;
+
+// s_waitcnt immediates: vmcnt(0) and vmcnt(16), lgkmcnt and expcnt untouched
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+// workgroup barrier without memory fences; the compiler may move no memory
+// access across it
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kLdsWaves *kWave, 1) void gemm_big_kernel(GemmArgs a) {
+    using T = bf16_t;
+    __shared__ u32x4 sm[2][2][16 * 128];   // [buffer][W, X][tile * 128 + row * 8 + slot]
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lid = (int)xcd_logical_id(blockIdx.x, gridDim.x);
+    const int mg = lid % a.MG, s = (lid / a.MG) % a.S, rb = lid / (a.MG * a.S);
+    const int n0 = rb * kBigTile, m0 = mg * kBigTile;
+    const int M = a.M, N = a.N, K = a.K, xT = a.xT, xsh = a.xsh;
+    const int NST = K / kBigSK;
+    const int sb = NST * s / a.S, se = NST * (s + 1) / a.S;   // se - sb >= 2
+
+    // load instruction i of this wave: tile rows 8 (wave + 4 i) .. + 7, one
+    // per 8 lanes; byte offsets from the segment (W) or X base.  The 8 rows
+    // share a segment (segments start at multiples of 64); rows past N or M
+    // read the last row, whose products are never stored.
+    const char *wseg[8];
+    uint32_t wo[8], xo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r0 = n0 + 8 * (wave + 4 * i);
+        const int nsel = r0 < N ? r0 : N - 1;
+        const int segbeg = nsel >= a.end1 ? a.end1 : (nsel >= a.end0 ? a.end0 : 0);
+        wseg[i] = (const char *)(nsel >= a.end1 ? a.W2 : (nsel >= a.end0 ? a.W1 : a.W0));
+        const int row = 8 * (wave + 4 * i) + lane / 8;
+        const int chunk = (lane % 8) ^ ((row % 16) >> 1);
+        int n = n0 + row;
+        n = n < N ? n : N - 1;
+        wo[i] = ((uint32_t)(n - segbeg) * (uint32_t)K + chunk * 8) * 2u;
+        int m = m0 + row;
+        m = m < M ? m : M - 1;
+        xo[i] = (uint32_t)((x_row<T>(a, m) - (const T *)a.X) + chunk * 8) * 2u;
+    }
+    const char *Xb = (const char *)a.X;
+    // byte offset of stage st in an X row: x_off without a branch (the plain
+    // layout as a heads layout whose head is longer than any row)
+    const int xs = xT > 0 ? xsh : 30;
+    auto xstage = [&](int st) {
+        const uint32_t k = (uint32_t)st * kBigSK;
+        return 2u * ((((k >> xs) * (uint32_t)xT) << xs) + (k & ((1u << xs) - 1u)));
+    };
+    // load q (< 16) of stage st (X stage offset xk): operand q & 1, instruction q >> 1
+    auto dma = [&](int st, uint32_t xk, int q) {
+        const int b = st & 1, i = q >> 1;
+        if (q & 1)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Xb + (xo[i] + xk)),
+                                             (lds_ptr_t)&sm[b][1][(wave + 4 * i) * kWave], 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wseg[i] + (wo[i] + (uint32_t)st * 128u)),
+                                             (lds_ptr_t)&sm[b][0][(wave + 4 * i) * kWave], 16, 0, 0);
+    };
+    const int wn = (wave & 1) * 8, wm = (wave >> 1) * 8;
+    const int r16 = lane % 16, cg = lane / 16;
+    int fo[2];   // slot of this lane's fragment in k-step u
+#pragma unroll
+    for (int u = 0; u < 2; ++u) fo[u] = r16 * 8 + ((4 * u + cg) ^ (r16 >> 1));
+    // fragment q of k-step u of stage st: X tiles 0-7, then W tiles 0-7
+    auto rd1 = [&](u32x4 (&fw)[8], u32x4 (&fx)[8], int st, int u, int q) {
+        if (q < 8) fx[q] = sm[st & 1][1][(wm + q) * 128 + fo[u]];
+        else fw[q - 8] = sm[st & 1][0][(wn + q - 8) * 128 + fo[u]];
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mm = [&](const u32x4 (&fw)[8], const u32x4 (&fx)[8], int r0, int r1) {
+#pragma unroll
+        for (int r = r0; r < r1; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mma16_step(acc[r][j], fw[r], fx[j], T{});
+    };
+    u32x4 aw[8], ax[8], bw[8], bx[8];
+    // Entered with stage st in registers up to the first half of k-step 1
+    // (bw, bx) and stage st + 1 loaded: finishes stage st, reads and computes
+    // stage st + 1 up to the same point; loads stage st + 2 when `load`.  In
+    // 16 chunks of 8 products, fenced so that they issue in this order:
+    // chunks 0-3 the rest of stage st, reading k-step 0 of st + 1 (and the
+    // loads, 4 per chunk); 4-11 k-step 0 of st + 1, reading its k-step 1;
+    // 12-15 the first half of that.
+    auto body = [&](int st, bool load) {
+        const uint32_t xk = xstage(st + 2);
+        wait_vm0();      // stage st + 1: this wave's loads
+        lds_barrier();   // ... every wave's; every wave is done with stage st
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (load && c < 4) {
+#pragma unroll
+                for (int q = 4 * c; q < 4 * c + 4; ++q) dma(st + 2, xk, q);
+            }
+            if (c < 4) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rd1(aw, ax, st + 1, 0, 4 * c + q);
+                mm(bw, bx, 4 + c, 5 + c);
+            } else if (c < 12) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) rd1(bw, bx, st + 1, 1, 2 * (c - 4) + q);
+                mm(aw, ax, c - 4, c - 3);
+            } else {
+                mm(bw, bx, c - 12, c - 11);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dma(sb, xstage(sb), q);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dma(sb + 1, xstage(sb + 1), q);
+    wait_vm16();     // stage sb
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rd1(aw, ax, sb, 0, q);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rd1(bw, bx, sb, 1, q);
+    mm(aw, ax, 0, 8);
+    mm(bw, bx, 0, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    int st = sb;
+    for (; st + 2 < se; ++st) body(st, true);
+    body(st, false);   // st = se - 2
+    mm(bw, bx, 4, 8);
+    wait_vm0();
+    // lane holds Y[m0 + 16 (wm + j) + c][n0 + 16 (wn + r) + 4g .. + 3]
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            gemm_store(a, s, m0 + 16 * (wm + j) + r16, n0 + 16 * (wn + r) + 4 * cg, acc[r][j]);
+}
+
 // ---- epilogues
 // Y[i] (+)= sum over s < NS of part[s][i], s in order; four elements per
 // thread when n % 4 == 0.
@@ -549,19 +716,38 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(NormArgs a) {
 
 // ------------------------------------------------------------------ host
 struct GemmPlan {
-    bool staged;
+    bool big, staged;
     int S, MG, RB, MT;
     size_t part_bytes;   // partials needed (0 when written directly)
 };
 
-// The staged kernel when K is a whole number of stages and M > 16 (it pays
-// when X is read by many tiles); else the streaming kernel.  S splits of K
-// per row block when the row blocks alone leave most CUs idle, each split
-// keeping at least four stages (batches per wave); at most kMaxSplit.
-// need_part forces partials (an epilogue reads them).
-inline GemmPlan gemm_plan(int M, int N, int K, int kstep, bool need_part) {
+// The large kernel for bf16 with more than kBigMinRows rows and K a whole
+// number of its stages; else the staged kernel when K is a whole number of
+// stages and M > 16 (it pays when X is read by many tiles); else the
+// streaming kernel.  S splits of K per tile when the tiles alone leave most
+// CUs idle (the large kernel: as many as fit in one round of the CUs), each
+// split keeping at least four stages (batches per wave, eight stages for
+// the large kernel); at most kMaxSplit.  need_part forces partials (an
+// epilogue reads them).
+inline GemmPlan gemm_plan(int M, int N, int K, int kstep, bool bf16, bool need_part) {
     GemmPlan g;
     const int KS = K / kstep;
+    // (32-bit byte offsets in the large kernel: N K < 2^31)
+    g.big = bf16 && M > kBigMinRows && K % kBigSK == 0 && K / kBigSK >= 2 &&
+            (long long)N * K < (1LL << 31);
+    if (g.big) {
+        g.staged = false;
+        g.MT = 0;
+        g.RB = (N + kBigTile - 1) / kBigTile;
+        g.MG = (M + kBigTile - 1) / kBigTile;
+        const int units = g.RB * g.MG, smax = K / kBigSK / 8;
+        int S = units >= 3 * kNumCU / 4 ? 1 : kNumCU / units;
+        S = S < smax ? S : smax;
+        S = S < kMaxSplit ? S : kMaxSplit;
+        g.S = S > 1 ? S : 1;
+        g.part_bytes = (need_part || g.S > 1) ? (size_t)g.S * M * N * 4 : 0;
+        return g;
+    }
     const int mt = M >= kGemmCols ? 4 : (M + 15) / 16;
     g.staged = mt >= 2 && KS % kLdsU == 0;
     // staged with more than 64 rows: 128 X rows per workgroup (W read from
@@ -598,9 +784,10 @@ inline FwdLayout fwd_layout(int B, int T, int d, int Hq, int Hkv, int dh, int Lc
                             int dtype) {
     const int M = B * T, es = dtype == MEDUSA_BF16 ? 2 : 4, kstep = dtype == MEDUSA_BF16 ? 32 : 16;
     FwdLayout L;
-    L.qkv = gemm_plan(M, (Hq + 2 * Hkv) * dh, d, kstep, true);
-    L.wo = gemm_plan(M, d, Hq * dh, kstep, false);
-    L.lm = gemm_plan(M, V, d, kstep, false);
+    const bool bf16 = dtype == MEDUSA_BF16;
+    L.qkv = gemm_plan(M, (Hq + 2 * Hkv) * dh, d, kstep, bf16, true);
+    L.wo = gemm_plan(M, d, Hq * dh, kstep, bf16, false);
+    L.lm = gemm_plan(M, V, d, kstep, bf16, false);
     size_t part = L.qkv.part_bytes;
     part = part > L.wo.part_bytes ? part : L.wo.part_bytes;
     part = part > L.lm.part_bytes ? part : L.lm.part_bytes;
@@ -631,7 +818,11 @@ inline unsigned grid_for(size_t n, int threads) {
 
 template <typename T, int MT>
 void launch_gemm_kernel(const GemmPlan &g, const GemmArgs &a, hipStream_t st) {
-    if (g.staged)
+    if (g.big) {
+        if constexpr (std::is_same<T, bf16_t>::value)
+            hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)(g.RB * g.S * g.MG)),
+                               dim3(kLdsWaves * kWave), 0, st, a);
+    } else if (g.staged)
         hipLaunchKernelGGL((gemm_lds_kernel<T, MT < 2 ? 2 : MT>), dim3((unsigned)(g.RB * g.S * g.MG)),
                            dim3(kLdsWaves * kWave), 0, st, a);
     else

@@ -162,3 +162,15 @@ def test_forward_max_tree():
     assert t.T == 256
     I = W.forward_inputs(wl, 2, T=t.T)
     _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
+
+
+def test_forward_large_tiles_ragged():
+    """333 rows (one full 256-row tile and a ragged one), d = 1024 so that
+    every projection splits K in two (fp32 partials), q/k/v segments inside
+    one 256-row W tile, the output projection reading the heads layout, and
+    V = 1000 (a ragged last W tile)."""
+    wl = _wl("ragged_b16_gqa_typical", cid=36, B=3, d=1024, V=1000, Hq=8, Hkv=2, dh=128, L_lo=0,
+             L_hi=60)
+    t = W.random_tree(11, 111, 5, 3)
+    I = W.forward_inputs(wl, 2, T=t.T)
+    _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
