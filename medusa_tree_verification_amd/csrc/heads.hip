@@ -140,57 +140,44 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
 }
 
 // ------------------------------------------------------------- top-s lists
+template <int SM>
 struct TopList {
-    float v[kSMax];
-    int id[kSMax];
+    float v[SM];
+    int id[SM];
     __device__ void clear() {
 #pragma unroll
-        for (int r = 0; r < kSMax; ++r) {
+        for (int r = 0; r < SM; ++r) {
             v[r] = -INFINITY;
             id[r] = 0x7FFFFFFF;
         }
     }
-    // the s-th entry (the admission bar), read without dynamic indexing
-    __device__ void bar(int s, float &bv, int &bi) const {
-        bv = v[0];
-        bi = id[0];
-#pragma unroll
-        for (int r = 1; r < kSMax; ++r)
-            if (r == s - 1) {
-                bv = v[r];
-                bi = id[r];
-            }
-    }
-    // insert keeping the first s entries sorted; entries past s stay sentinels
+    // insert keeping the first s entries sorted; entries past s stay
+    // sentinels.  Branch-free: entry r keeps its place while it is ahead of
+    // x (a prefix of the list, which is sorted); the first one that is not
+    // gives its place to x and the ones after it move down, the s-th
+    // dropping out.  A candidate behind all s entries changes nothing.
     __device__ void insert(float x, int i, int s) {
-        float bv;
-        int bi;
-        bar(s, bv, bi);
-        if (!cand_before(x, i, bv, bi)) return;
+        bool keep[SM];
 #pragma unroll
-        for (int r = kSMax - 1; r >= 0; --r) {
-            if (r >= s) continue;
-            const bool here_better = cand_before(x, i, v[r], id[r]);
-            const bool above_better = r == 0 || cand_before(x, i, v[r > 0 ? r - 1 : 0], id[r > 0 ? r - 1 : 0]);
-            if (here_better) {
-                if (above_better && r > 0) {  // x moves further up: shift entry r-1 down
-                    v[r] = v[r - 1];
-                    id[r] = id[r - 1];
-                } else {                      // x lands here
-                    v[r] = x;
-                    id[r] = i;
-                }
-            }
+        for (int r = 0; r < SM; ++r) keep[r] = r >= s || cand_before(v[r], id[r], x, i);
+#pragma unroll
+        for (int r = SM - 1; r > 0; --r) {   // downwards: v[r - 1] is still the old entry
+            const float nv = keep[r] ? v[r] : (keep[r - 1] ? x : v[r - 1]);
+            const int ni = keep[r] ? id[r] : (keep[r - 1] ? i : id[r - 1]);
+            v[r] = nv;
+            id[r] = ni;
         }
+        v[0] = keep[0] ? v[0] : x;
+        id[0] = keep[0] ? id[0] : i;
     }
     __device__ void pop() {
 #pragma unroll
-        for (int r = 0; r < kSMax - 1; ++r) {
+        for (int r = 0; r < SM - 1; ++r) {
             v[r] = v[r + 1];
             id[r] = id[r + 1];
         }
-        v[kSMax - 1] = -INFINITY;
-        id[kSMax - 1] = 0x7FFFFFFF;
+        v[SM - 1] = -INFINITY;
+        id[SM - 1] = 0x7FFFFFFF;
     }
 };
 
@@ -199,12 +186,13 @@ struct TopList {
 // wave).  Afterwards every lane of a group holds in ov/oi the best s of the
 // union of its group's lists.  Lists are consumed.  Ids within a group are
 // distinct.
-__device__ void group_merge(TopList &L, int s, int m0, float (&ov)[kSMax], int (&oi)[kSMax]) {
+template <int SM>
+__device__ void group_merge(TopList<SM> &L, int s, int m0, float (&ov)[kSMax], int (&oi)[kSMax]) {
 #pragma unroll
     for (int r = 0; r < kSMax; ++r) {
         ov[r] = -INFINITY;
         oi[r] = 0x7FFFFFFF;
-        if (r >= s) continue;
+        if (r >= s || r >= SM) continue;
         float bv = L.v[0];
         int bi = L.id[0];
         for (int m = m0; m < kWave; m <<= 1) {
@@ -274,6 +262,7 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
 // Merge the partial top-s lists of head `head` (one per workgroup owning a
 // tile of it) into topk_ids / topk_vals: wave `wave` of workgroup row
 // blockIdx.y takes column blockIdx.y * kS2Waves + wave.
+template <int SM>
 __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part,
                                                  int32_t *__restrict__ topk_ids,
                                                  float *__restrict__ topk_vals,
@@ -287,7 +276,7 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
     const int nparts = wg_last - wg_first + 1;
     const int col = (int)blockIdx.y * kS2Waves + wave;   // one wave per (head, column)
     if (col < B) {
-        TopList M;
+        TopList<SM> M;
         M.clear();
         const float2 *src = part + ((size_t)head * B + col) * P * kSMax;
         for (int p0 = 0; p0 < nparts; p0 += kWave) {
@@ -324,7 +313,7 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
 
 // LM: the LM head rides along as head K (a separate instantiation, so the
 // plain and the root-token streams show up as different kernels in traces).
-template <typename T, bool LM>
+template <typename T, bool LM, int SM>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, const T *__restrict__ w_lm,
     const T *__restrict__ hidden, float *__restrict__ logits_out, float2 *__restrict__ part, int B,
@@ -353,7 +342,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     __syncthreads();
 
     const bool bcol = c < B;
-    TopList L;
+    TopList<SM> L;
     L.clear();
     int cur_head = tile < wend ? tile / ntph : -1;
 
@@ -466,11 +455,12 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
 
 // The final top-s of one head: the per-workgroup partial lists of the
 // workgroups that own its tiles, merged with one wave per column.
+template <int SM>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_merge_kernel(
     const float2 *__restrict__ part, int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals,
     int32_t *__restrict__ root_token, float *__restrict__ root_val, int B, int K, int s, int ntph,
     int nt, int P) {
-    merge_head_lists(part, topk_ids, topk_vals, root_token, root_val, (int)blockIdx.x, B, K, s,
+    merge_head_lists<SM>(part, topk_ids, topk_vals, root_token, root_val, (int)blockIdx.x, B, K, s,
                      ntph, nt, P, (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
 }
 
@@ -517,14 +507,18 @@ int launch_stage2_stream(const void *w2, const void *w_lm, const void *hidden, i
     float2 *part = (float2 *)(base + L.part_off);
     const dim3 grid((unsigned)L.P), block(kS2Waves * kWave);
     const bool lm = w_lm != nullptr;
+    // lists of 4 when s <= 4 (every insert costs its capacity)
+    const bool s4 = s <= 4;
     if (dtype == MEDUSA_BF16) {
-        auto *kern = lm ? heads_stage2_kernel<bf16_t, true> : heads_stage2_kernel<bf16_t, false>;
+        auto *kern = lm ? (s4 ? heads_stage2_kernel<bf16_t, true, 4> : heads_stage2_kernel<bf16_t, true, kSMax>)
+                        : (s4 ? heads_stage2_kernel<bf16_t, false, 4> : heads_stage2_kernel<bf16_t, false, kSMax>);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)w2,
                            (const bf16_t *)(base + L.z_off), (const bf16_t *)w_lm,
                            (const bf16_t *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
                            L.P);
     } else {
-        auto *kern = lm ? heads_stage2_kernel<float, true> : heads_stage2_kernel<float, false>;
+        auto *kern = lm ? (s4 ? heads_stage2_kernel<float, true, 4> : heads_stage2_kernel<float, true, kSMax>)
+                        : (s4 ? heads_stage2_kernel<float, false, 4> : heads_stage2_kernel<float, false, kSMax>);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)w2,
                            (const float *)(base + L.z_off), (const float *)w_lm,
                            (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
@@ -540,7 +534,7 @@ int launch_stage2_merge(bool lm, int B, int K, int d, int V, int s, int dtype, i
                         hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype, lm);
     const float2 *part = (const float2 *)((char *)ws + L.part_off);
-    hipLaunchKernelGGL(heads_merge_kernel,
+    hipLaunchKernelGGL(s <= 4 ? heads_merge_kernel<4> : heads_merge_kernel<kSMax>,
                        dim3((unsigned)L.nh, (unsigned)((B + kS2Waves - 1) / kS2Waves)),
                        dim3(kS2Waves * kWave), 0, st, part, topk_ids, topk_vals, root_token,
                        root_val, B, K, s, L.ntph, L.nt, L.P);

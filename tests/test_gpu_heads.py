@@ -40,6 +40,8 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05):
     (1, 1, 128, 16, 1),        # one tile
     (1, 3, 256, 1000, 2),      # ragged last tile
     (3, 2, 384, 777, 8),       # s = 8, odd batch
+    (2, 3, 256, 2000, 4),      # s = 4: every slot of the short lists
+    (5, 2, 256, 1500, 5),      # s = 5: the long lists
     (16, 5, 256, 4099, 3),     # full batch tile, tiles spanning head boundaries
     (7, 4, 128, 70000, 3),     # many tiles per workgroup
 ])
