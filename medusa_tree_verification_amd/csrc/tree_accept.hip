@@ -121,38 +121,64 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
     return r;
 }
 
+// Argmax over 16-byte chunks: the best chunk's maximum, its first element
+// index and raw bits, resolved to an element index once at the end (fewer
+// operations per element than tracking the index of every element).  The
+// first chunk is always taken; later ones only when strictly larger, so on
+// ties the earlier chunk, and within it the earlier element, wins.
+struct ChunkArgMax {
+    float v;
+    int base;      // element index of the chunk's first element; -1: none yet
+    u32x4 bits;
+    __device__ __forceinline__ void add(const u32x4 &c, float cm, int b) {
+        const bool take = base < 0 || cm > v;
+        v = take ? cm : v;
+        base = take ? b : base;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) bits[w] = take ? c[w] : bits[w];
+    }
+    template <typename T>
+    __device__ __forceinline__ void resolve(ArgMax &am) const {
+        if (base < 0) return;
+        constexpr int E = Elem<T>::kPer16B;
+        int e0 = E - 1;
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e) e0 = chunk_elem<T>(bits, e) == v ? e : e0;
+        am.add(v, base + e0);
+    }
+};
+
+// One 16-byte chunk (E elements from index base): argmax, and (typical) the
+// softmax statistics of x * zs with one fused multiply-add per element.
 template <typename T>
-__device__ __forceinline__ void add_chunk(const u32x4 &c, int base, bool typical, float zs,
-                                          ArgMax &am, SoftStats &st) {
+__device__ __forceinline__ void add_chunk_fast(const u32x4 &c, int base, bool typical, float zs,
+                                               ChunkArgMax &cam, SoftStats &st) {
     constexpr int E = Elem<T>::kPer16B;
     float x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        x[e] = chunk_elem<T>(c, e);
-        am.add(x[e], base + e);
-    }
-    if (typical) {
-        float cm = -INFINITY;
+    for (int e = 0; e < E; ++e) x[e] = chunk_elem<T>(c, e);
+    float cm = x[0];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            x[e] *= zs;
-            cm = fmaxf(cm, x[e]);
-        }
-        if (cm > st.m) {
-            const float d = st.m - cm;
+    for (int e = 1; e < E; ++e) cm = fmaxf(cm, x[e]);
+    cam.add(c, cm, base);
+    if (typical) {
+        const float cms = cm * zs;   // zs > 0: the maximum of the scaled chunk
+        if (cms > st.m) {
+            const float d = st.m - cms;
             if (st.S != 0.f) {
                 const float f = fast_exp2(d);
                 st.A = (st.A + d * st.S) * f;
                 st.S *= f;
             }
-            st.m = cm;
+            st.m = cms;
         }
+        const float nm = -st.m;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float dd = x[e] - st.m;
+            const float dd = fmaf(x[e], zs, nm);
             const float ex = fast_exp2(dd);
             st.S += ex;
-            st.A += ex * dd;
+            st.A = fmaf(ex, dd, st.A);
         }
     }
 }
@@ -182,6 +208,7 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
     const auto rs = make_rsrc(row + lo, (uint32_t)(hi - lo) * (uint32_t)sizeof(T));
     if ((V % E) == 0 && (lo % E) == 0 && (hi % E) == 0) {
         const int nch = (hi - lo) / E;
+        ChunkArgMax cam{-INFINITY, -1, u32x4{0u, 0u, 0u, 0u}};
         for (int base = (int)threadIdx.x; base < nch; base += U * NT) {
             u32x4 c[U];
 #pragma unroll
@@ -189,9 +216,10 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int ch = base + u * NT;
-                if (ch < nch) add_chunk<T>(c[u], lo + ch * E, typical, zs, am, st);
+                if (ch < nch) add_chunk_fast<T>(c[u], lo + ch * E, typical, zs, cam, st);
             }
         }
+        cam.resolve<T>(am);
     } else {
         const int n = hi - lo;
         for (int base = (int)threadIdx.x; base < n; base += U * NT) {
