@@ -174,3 +174,15 @@ def test_forward_large_tiles_ragged():
     t = W.random_tree(11, 111, 5, 3)
     I = W.forward_inputs(wl, 2, T=t.T)
     _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
+
+
+def test_forward_large_tiles_minimum_sizes():
+    """The 256-row-tile path at its smallest: 258 rows (a second tile with
+    two live rows), d = 128 and Hq * dh = 128 (two 64-k stages, so the
+    stage loop runs once without loading), dh = 64 (one stage per head of
+    the output projection's input) and V = 70 (one W tile, mostly past N)."""
+    wl = _wl("ragged_b16_gqa_typical", cid=37, B=3, d=128, V=70, Hq=2, Hkv=1, dh=64, L_lo=1,
+             L_hi=40)
+    t = W.random_tree(13, 86, 5, 3)
+    I = W.forward_inputs(wl, 2, T=t.T)
+    _compare(_gpu(I, t.parent, wl), _oracle(I, t.parent, wl), wl.dtype)
