@@ -42,6 +42,9 @@ def parse():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle timing")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB read before each step of the per-call breakdown pass, outside "
+                         "its events (more than the last-level cache and the L2s; 0: none)")
     ap.add_argument("--forward-blocks", type=int, default=4,
                     help="attention blocks of the synthetic verify forward (a next-row timing)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -209,9 +212,18 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # each step of this pass starts with cold caches: a buffer larger than the
+    # last-level cache is read (a sum) before the step's first event.  A read
+    # leaves no dirty lines: after a written flush their write-back ran into
+    # the step's first kernels.
+    flush = torch.ones(args.flush_mib << 17, dtype=torch.int64, device=dev) if args.flush_mib > 0 else None
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
     for i in range(args.steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
         step(evs[i])
     torch.cuda.synchronize()
+    del flush, sink
     names = ["heads_stage1", "heads_stage2", "heads_merge", "tree_attention", "tree_accept"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in
            enumerate(names)}
