@@ -29,7 +29,7 @@ namespace medusa {
 namespace {
 
 #ifndef MEDUSA_ATTN_MIN_CHUNK
-#define MEDUSA_ATTN_MIN_CHUNK 256
+#define MEDUSA_ATTN_MIN_CHUNK 384
 #endif
 #ifndef MEDUSA_ATTN_WG_PER_CU
 #define MEDUSA_ATTN_WG_PER_CU 1
