@@ -102,6 +102,11 @@ struct StageCopy {
     static constexpr int NK = (kBN * C::CPR) / NT;                   // K chunks / thread
     static_assert((kBN * C::CPR) % NT == 0, "K chunks divide evenly over the threads");
     static constexpr int NV = ((kBN / 4) * C::CPR + NT - 1) / NT;    // V units / thread
+    // With twice as many threads as V units, the units go to the upper half
+    // of the workgroup (waves NW/2 ..): the two waves of a SIMD then start a
+    // stage's matrix and vector phases apart, by the transposing stores.
+    static constexpr bool kVUpper = (kBN / 4) * C::CPR * 2 == NT;
+    __device__ __forceinline__ static int vthread(int tid) { return kVUpper ? tid ^ (NT / 2) : tid; }
     u32x4 k[NK];
     u32x4 v[NV][4];
 
@@ -117,7 +122,7 @@ struct StageCopy {
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int u = tid + i * NT;
+            const int u = vthread(tid) + i * NT;
             const int kg = u % (kBN / 4), col = u / (kBN / 4);   // see store()
             const bool live = u < (kBN / 4) * C::CPR;   // spare threads: offsets past the
                                                        // range, dropped by the hardware
@@ -144,7 +149,7 @@ struct StageCopy {
         // 4-key slots of one dh row (128 contiguous bytes, no bank conflicts).
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int u = tid + i * NT;
+            const int u = vthread(tid) + i * NT;
             if (u >= (kBN / 4) * C::CPR) continue;
             const int kg = u % (kBN / 4), col = u / (kBN / 4);
             const int pos = vt_pos<T>(4 * kg);
@@ -392,10 +397,11 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
         const uint32_t nbytes = (uint32_t)(nv * DH * (int)sizeof(T));
         dst.load(make_rsrc(kb, nbytes), make_rsrc(vb, nbytes), tid);
     };
-    // Double-buffered LDS stages, one barrier each: stage i is computed from
-    // buffer i%2, then stage i+1 (loads issued PD stages earlier) is written
-    // to the other buffer and the loads of stage i+1+PD go out into the
-    // register set it freed.  The loop is unrolled by PD so that every
+    // Double-buffered LDS stages, one barrier each: stage i+1 (loads issued
+    // PD stages earlier) is written to buffer (i+1)%2, free since the last
+    // barrier, the loads of stage i+1+PD go out into the register set it
+    // freed, and stage i is computed from buffer i%2.  Staging first lets the
+    // waves without V units start computing while the others transpose V.  The loop is unrolled by PD so that every
     // register set is named statically; it runs a multiple of PD stages, the
     // ones past the last computing nothing.
     // prologue: stages 0 .. PD-1 in flight, stage 0 to LDS, stage PD issued
@@ -409,6 +415,8 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
 #pragma unroll
         for (int k = 0; k < PD; ++k) {   // unrolled: register set (k + 1) % PD is static
             const int sidx = base + k;
+            cp[(k + 1) % PD].store(lds[(sidx + 1) & 1], tid);
+            issue(cp[(k + 1) % PD], sidx + 1 + PD);
             if (computes && sidx < nstage) {
                 int kind = 0, klim = kBN;
                 uint64_t mword = 0ull;
@@ -424,8 +432,6 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
                 attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword,
                                     cscale, sub_lo, sub_hi);
             }
-            cp[(k + 1) % PD].store(lds[(sidx + 1) & 1], tid);
-            issue(cp[(k + 1) % PD], sidx + 1 + PD);
             __syncthreads();
         }
     }
@@ -619,12 +625,11 @@ int check_attn(const void *q, const void *kc, const void *vc, const int32_t *pl,
 
 template <typename T, int DH>
 int launch_attn(const AttnParams &p, hipStream_t st) {
-    // at least four waves per workgroup so that staging a K/V block takes
-    // few loads per thread; waves beyond ks * W only help staging
-    if (p.ks * p.W <= 4)
-        hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, 4>), dim3(p.nwg), dim3(4 * kWave), 0, st, p);
-    else
-        hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, 8>), dim3(p.nwg), dim3(8 * kWave), 0, st, p);
+    // Eight waves (two per SIMD at <= 256 registers each): with few row
+    // waves (ks * W <= 4) the others only stage K/V, which measured faster
+    // than four waves at one per SIMD.
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, kMaxWaves>), dim3(p.nwg), dim3(kMaxWaves * kWave),
+                       0, st, p);
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (p.nsplit > 1) {
         const size_t rows = (size_t)p.B * p.Hq * p.T;
