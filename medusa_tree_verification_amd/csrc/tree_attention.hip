@@ -157,11 +157,13 @@ struct StageCopy {
             for (int e = 0; e < C::KC; ++e) {
                 char *dst = Vt + (col * C::KC + e) * C::VT_STRIDE + pos * (int)sizeof(T);
                 if constexpr (sizeof(T) == 2) {
-                    const int w = e >> 1, sh = (e & 1) * 16;
-                    const uint32_t lo = ((v[i][0][w] >> sh) & 0xFFFFu) |
-                                        (((v[i][1][w] >> sh) & 0xFFFFu) << 16);
-                    const uint32_t hi = ((v[i][2][w] >> sh) & 0xFFFFu) |
-                                        (((v[i][3][w] >> sh) & 0xFFFFu) << 16);
+                    // element e of four keys: the low or high halves of word
+                    // e/2, paired by byte selects (v_perm_b32: selector bytes
+                    // 0-3 pick the second operand's bytes, 4-7 the first's)
+                    const int w = e >> 1;
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(v[i][1][w], v[i][0][w], sel);
+                    const uint32_t hi = __builtin_amdgcn_perm(v[i][3][w], v[i][2][w], sel);
                     *reinterpret_cast<u32x2 *>(dst) = u32x2{lo, hi};
                 } else {
                     st16(dst, u32x4{v[i][0][e], v[i][1][e], v[i][2][e], v[i][3][e]});
