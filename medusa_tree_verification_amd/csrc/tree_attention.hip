@@ -503,8 +503,9 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
 }
 
 // Merge split partials of the rows whose prefix used more than one split:
-// one wave per row; lane j holds split j's (max, sum) (64 splits per round),
-// then the O partials are read with kCombU splits of loads in flight.
+// one wave per row; lane j holds split j's (max, sum).  Up to kCombU splits
+// every load goes out in one round; past that, 64 splits' (max, sum) per
+// round, then the O partials with kCombU splits of loads in flight.
 constexpr int kCombU = 8;
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
@@ -513,6 +514,49 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     const size_t nrows = (size_t)p.B * p.Hq * p.T;
     if (rowid >= nrows) return;
     const int b = (int)(rowid / ((size_t)p.Hq * p.T));
+    constexpr int PER = DH / kWave;
+    if (p.nsplit <= kCombU) {
+        // One round of loads: the prefix length, every split's (max, sum)
+        // (lane j: split j) and O partials are all issued before any wait.
+        // Splits past the row's own count were never written: they are
+        // skipped, not weighted by zero (their bytes may be NaN).
+        const int j = lane < p.nsplit ? lane : 0;
+        const float2 ml = p.part_ml[(size_t)j * nrows + rowid];
+        float v[kCombU][PER];
+#pragma unroll
+        for (int u = 0; u < kCombU; ++u) {
+            const int sp = u < p.nsplit ? u : 0;
+            const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+        }
+        int L = p.prefix_len[b];
+        L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+        const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+        if (nsb == 1) return;
+        const bool live = lane < nsb;
+        float mmax = live ? ml.x : -INFINITY;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, m));
+        const float w = live ? fast_exp2(ml.x - mmax) : 0.f;
+        float den = live ? w * ml.y : 0.f;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m);
+        float acc[PER] = {};
+#pragma unroll
+        for (int u = 0; u < kCombU; ++u) {
+            const float wu = __shfl(w, u);
+            if (u < nsb) {   // the same in every lane
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += wu * v[u][e];
+            }
+        }
+        const float inv = 1.0f / den;
+        T *dst = (T *)p.out + rowid * DH;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) dst[lane * PER + e] = Elem<T>::from_f32(acc[e] * inv);
+        return;
+    }
     int L = p.prefix_len[b];
     L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
     const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
@@ -524,7 +568,6 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, m));
-    constexpr int PER = DH / kWave;
     float acc[PER] = {};
     float den = 0.f;
     for (int s0 = 0; s0 < nsb; s0 += kWave) {
