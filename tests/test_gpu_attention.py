@@ -89,6 +89,18 @@ def test_attention_gqa_groups(G, T):
     _check(x, t.parent, 1 / math.sqrt(dh), "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_attention_row_wave_counts(G, dtype):
+    # G * 30 query rows per kv head: 1 .. 8 row waves of 32, i.e. every
+    # split of the eight waves between row owners (one or two per row tile)
+    # and waves that only stage K/V; ragged prefixes over several splits
+    t = W.random_tree(60 + G, 30, 4, 3)
+    B, Hkv, dh, Lcap = 2, 2, 128, 700
+    x = _inputs(350 + G, B, G * Hkv, Hkv, t.T, dh, Lcap, [700, 389], dtype)
+    _check(x, t.parent, 1 / math.sqrt(dh), dtype)
+
+
 def test_attention_long_prefix_many_splits():
     t = TREES["full121"]
     B, Hq, Hkv, dh, Lcap = 1, 4, 1, 128, 20000
