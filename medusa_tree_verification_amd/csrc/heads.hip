@@ -72,23 +72,32 @@ inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype, int lm = 
 }
 
 // ------------------------------------------------------------------ stage 1
-template <typename T>
+// A workgroup owns NT consecutive 16-row tiles of the K*d row space (at
+// most 64 rows: one head, since d % 128 == 0); each of its waves streams them
+// over a quarter of d, so that every hidden-state fragment it loads feeds NT
+// MFMAs (with 16 sequences those loads touch 16 rows each).  The quarters
+// are summed in LDS in a fixed order and wave r finishes tile r.
+template <typename T, int NT>
 __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
     const T *__restrict__ hidden, const T *__restrict__ w1, T *__restrict__ z, int B, int K,
     int d) {
     constexpr int KC = Elem<T>::kPer16B;  // elements per lane per k-step
     constexpr int KSTEP = 4 * KC;         // k per step (4 lane groups)
-    __shared__ f32x4 red[kS1Waves][kWave];
+    static_assert(NT >= 1 && NT <= kS1Waves, "wave r finishes tile r");
+    __shared__ f32x4 red[kS1Waves][NT][kWave];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int g = lane / 16, c = lane % 16;
-    const int tile = blockIdx.x;                 // 16 rows of the K*d row space
-    const int head = (tile * 16) / d;
-    const int row0 = tile * 16 - head * d;      // first row within the head
+    const int tile0 = blockIdx.x * NT;           // first tile of the workgroup
+    const int head = (tile0 * 16) / d;
+    const int row0 = tile0 * 16 - head * d;     // its first row within the head
 
     const int kspan = d / kS1Waves;
     const int kbeg = wave * kspan;
-    const T *arow = w1 + ((size_t)head * d + row0 + c) * (size_t)d + kbeg + g * KC;
+    const T *arow[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r)
+        arow[r] = w1 + ((size_t)head * d + row0 + r * 16 + c) * (size_t)d + kbeg + g * KC;
     // lanes of columns >= B read column B-1: their outputs are never used, and
     // an unconditional load keeps the loop free of exec-mask branches
     const bool bcol = c < B;
@@ -98,41 +107,48 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
     // covers whole groups of kS1Unroll steps, the tail loop the rest.
     // Batches start at a per-wave rotated offset (spreads lockstep waves over
     // HBM channels); loads of a batch are issued ahead of its MFMAs.
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int KB = KSTEP * kS1Unroll;
     const int nb = kspan / KB;
     int bi = nb > 0 ? (int)((blockIdx.x * kS1Waves + wave) % (unsigned)nb) : 0;
     for (int i = 0; i < nb; ++i) {
         const int kb = bi * KB;
         bi = bi + 1 == nb ? 0 : bi + 1;
-        u32x4 a[kS1Unroll], b[kS1Unroll];
+        u32x4 a[NT][kS1Unroll], b[kS1Unroll];
 #pragma unroll
-        for (int u = 0; u < kS1Unroll; ++u) {
-            a[u] = ld16(arow + kb + u * KSTEP);
-            b[u] = ld16(brow + kb + u * KSTEP);
-        }
+        for (int u = 0; u < kS1Unroll; ++u) b[u] = ld16(brow + kb + u * KSTEP);
+#pragma unroll
+        for (int r = 0; r < NT; ++r)
+#pragma unroll
+            for (int u = 0; u < kS1Unroll; ++u) a[r][u] = ld16(arow[r] + kb + u * KSTEP);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kS1Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
+        for (int u = 0; u < kS1Unroll; ++u)
+#pragma unroll
+            for (int r = 0; r < NT; ++r) mma16_step(acc[r], a[r][u], b[u], T{});
     }
     for (int k0 = nb * KB; k0 < kspan; k0 += KSTEP) {
-        const u32x4 a = ld16(arow + k0);
         const u32x4 b = ld16(brow + k0);
-        mma16_step(acc, a, b, T{});
-    }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    f32x4 u = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < kS1Waves; ++w) u += red[w][lane];
+        for (int r = 0; r < NT; ++r) mma16_step(acc[r], ld16(arow[r] + k0), b, T{});
+    }
+#pragma unroll
+    for (int r = 0; r < NT; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    const int r = wave;
+    if (r >= NT) return;
+    f32x4 u = red[0][r][lane];
+#pragma unroll
+    for (int w = 1; w < kS1Waves; ++w) u += red[w][r][lane];
     if (!bcol) return;
-    // lane holds rows row0 + 4g + i of column (sequence) c
+    // lane holds rows row0 + 16r + 4g + i of column (sequence) c
     const T *hrow = hidden + (size_t)c * d;
-    T *zrow = z + ((size_t)c * K + head) * d + row0 + 4 * g;
+    T *zrow = z + ((size_t)c * K + head) * d + row0 + r * 16 + 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int j = row0 + 4 * g + i;
+        const int j = row0 + r * 16 + 4 * g + i;
         const float x = u[i];
         const float silu = x / (1.0f + expf(-x));
         zrow[i] = Elem<T>::from_f32(silu + Elem<T>::to_f32(hrow[j]));
@@ -486,13 +502,22 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
                   void *ws, hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype);
     char *base = (char *)ws;
-    const dim3 grid((unsigned)((size_t)K * d / 16)), block(kS1Waves * kWave);
-    if (dtype == MEDUSA_BF16)
-        hipLaunchKernelGGL(heads_stage1_kernel<bf16_t>, grid, block, 0, st, (const bf16_t *)hidden,
-                           (const bf16_t *)w1, (bf16_t *)(base + L.z_off), B, K, d);
-    else
-        hipLaunchKernelGGL(heads_stage1_kernel<float>, grid, block, 0, st, (const float *)hidden,
-                           (const float *)w1, (float *)(base + L.z_off), B, K, d);
+    // Four tiles per workgroup share the hidden-state loads, which pays from
+    // four sequences on (a single sequence's loads are one row, cheap) when
+    // the workgroups then fill the CUs evenly; otherwise one tile each, for
+    // a fine-grained grid (K = 5 heads: 320 four-tile groups on 256 CUs).
+    const size_t tiles = (size_t)K * d / 16;
+    const bool four = B >= 4 && (tiles / 4) % kNumCU == 0;
+    const dim3 grid((unsigned)(four ? tiles / 4 : tiles)), block(kS1Waves * kWave);
+    if (dtype == MEDUSA_BF16) {
+        auto *kern = four ? heads_stage1_kernel<bf16_t, 4> : heads_stage1_kernel<bf16_t, 1>;
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)hidden, (const bf16_t *)w1,
+                           (bf16_t *)(base + L.z_off), B, K, d);
+    } else {
+        auto *kern = four ? heads_stage1_kernel<float, 4> : heads_stage1_kernel<float, 1>;
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)hidden, (const float *)w1,
+                           (float *)(base + L.z_off), B, K, d);
+    }
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

@@ -53,6 +53,17 @@ def test_heads_random_shapes(dtype, B, K, d, V, s):
     assert amb <= max(1, B * K // 20)
 
 
+def test_heads_four_tile_stage1_partial_batch():
+    # K * d / 64 = 256 tile groups and B >= 4: stage 1 gives each workgroup
+    # four tiles; 6 of the 16 MFMA columns hold sequences
+    B, K, d, V, s = 6, 4, 4096, 300, 3
+    hx = _random_heads(4242, B, K, d, V, "bf16")
+    out = _run(hx, s, "bf16")
+    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "bf16")
+    amb = _compare(out, ref, s, "bf16")
+    assert amb <= 1
+
+
 def test_heads_exact_small_integers():
     """Values on a coarse binary grid make every fp32 sum exact: logits must be
     bit-identical to the oracle's."""
