@@ -525,10 +525,11 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
         float v[kCombU][PER];
 #pragma unroll
         for (int u = 0; u < kCombU; ++u) {
-            const int sp = u < p.nsplit ? u : 0;
-            const float *src = p.part_o + ((size_t)sp * nrows + rowid) * DH + lane * PER;
+            if (u < p.nsplit) {   // the same in every lane; v[u] is read only for u < nsb
+                const float *src = p.part_o + ((size_t)u * nrows + rowid) * DH + lane * PER;
 #pragma unroll
-            for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+                for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+            }
         }
         int L = p.prefix_len[b];
         L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
