@@ -72,32 +72,30 @@ inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype, int lm = 
 }
 
 // ------------------------------------------------------------------ stage 1
-// A workgroup owns NT consecutive 16-row tiles of the K*d row space (at
-// most 64 rows: one head, since d % 128 == 0); each of its waves streams them
-// over a quarter of d, so that every hidden-state fragment it loads feeds NT
-// MFMAs (with 16 sequences those loads touch 16 rows each).  The quarters
-// are summed in LDS in a fixed order and wave r finishes tile r.
+// A workgroup owns NT consecutive 16-row tiles of the K*d row space (the
+// heads' W1 rows are contiguous, so a group may cross from one head into the
+// next); each of its waves streams them over a quarter of d, so that every
+// hidden-state fragment it loads feeds NT MFMAs (with 16 sequences those
+// loads touch 16 rows each).  The quarters are summed in LDS in a fixed
+// order and wave w finishes tiles w, w + 4, ...
 template <typename T, int NT>
 __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
     const T *__restrict__ hidden, const T *__restrict__ w1, T *__restrict__ z, int B, int K,
     int d) {
     constexpr int KC = Elem<T>::kPer16B;  // elements per lane per k-step
     constexpr int KSTEP = 4 * KC;         // k per step (4 lane groups)
-    static_assert(NT >= 1 && NT <= kS1Waves, "wave r finishes tile r");
     __shared__ f32x4 red[kS1Waves][NT][kWave];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int g = lane / 16, c = lane % 16;
-    const int tile0 = blockIdx.x * NT;           // first tile of the workgroup
-    const int head = (tile0 * 16) / d;
-    const int row0 = tile0 * 16 - head * d;     // its first row within the head
+    const size_t row0 = (size_t)blockIdx.x * NT * 16;   // first row of the K*d row space
 
     const int kspan = d / kS1Waves;
     const int kbeg = wave * kspan;
     const T *arow[NT];
 #pragma unroll
     for (int r = 0; r < NT; ++r)
-        arow[r] = w1 + ((size_t)head * d + row0 + r * 16 + c) * (size_t)d + kbeg + g * KC;
+        arow[r] = w1 + (row0 + r * 16 + c) * (size_t)d + kbeg + g * KC;
     // lanes of columns >= B read column B-1: their outputs are never used, and
     // an unconditional load keeps the loop free of exec-mask branches
     const bool bcol = c < B;
@@ -137,21 +135,22 @@ __global__ __launch_bounds__(kS1Waves *kWave) void heads_stage1_kernel(
 #pragma unroll
     for (int r = 0; r < NT; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
-    const int r = wave;
-    if (r >= NT) return;
-    f32x4 u = red[0][r][lane];
-#pragma unroll
-    for (int w = 1; w < kS1Waves; ++w) u += red[w][r][lane];
     if (!bcol) return;
-    // lane holds rows row0 + 16r + 4g + i of column (sequence) c
     const T *hrow = hidden + (size_t)c * d;
-    T *zrow = z + ((size_t)c * K + head) * d + row0 + r * 16 + 4 * g;
+    for (int r = wave; r < NT; r += kS1Waves) {
+        f32x4 u = red[0][r][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = row0 + r * 16 + 4 * g + i;
-        const float x = u[i];
-        const float silu = x / (1.0f + expf(-x));
-        zrow[i] = Elem<T>::from_f32(silu + Elem<T>::to_f32(hrow[j]));
+        for (int w = 1; w < kS1Waves; ++w) u += red[w][r][lane];
+        // lane holds rows 4g + i of tile r, column (sequence) c
+        const size_t R = row0 + r * 16 + 4 * g;   // row in the K*d space (a tile stays in one head)
+        const int head = (int)(R / d), j0 = (int)(R % d);
+        T *zrow = z + ((size_t)c * K + head) * d + j0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = u[i];
+            const float silu = x / (1.0f + expf(-x));
+            zrow[i] = Elem<T>::from_f32(silu + Elem<T>::to_f32(hrow[j0 + i]));
+        }
     }
 }
 
@@ -502,19 +501,22 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
                   void *ws, hipStream_t st) {
     const HeadsLayout L = heads_layout(B, K, d, V, dtype);
     char *base = (char *)ws;
-    // Four tiles per workgroup share the hidden-state loads, which pays from
-    // four sequences on (a single sequence's loads are one row, cheap) when
-    // the workgroups then fill the CUs evenly; otherwise one tile each, for
-    // a fine-grained grid (K = 5 heads: 320 four-tile groups on 256 CUs).
+    // Four (or five) tiles per workgroup share the hidden-state loads, which
+    // pays from four sequences on (a single sequence's loads are one row,
+    // cheap) when the groups then fill the CUs evenly (K = 5 heads of 4096:
+    // 256 groups of five, where groups of four would leave a partial round);
+    // otherwise one tile each, for a fine-grained grid.
     const size_t tiles = (size_t)K * d / 16;
-    const bool four = B >= 4 && (tiles / 4) % kNumCU == 0;
-    const dim3 grid((unsigned)(four ? tiles / 4 : tiles)), block(kS1Waves * kWave);
+    const int nt = B < 4 ? 1 : (tiles / 4) % kNumCU == 0 ? 4 : (tiles / 5) % kNumCU == 0 && tiles % 5 == 0 ? 5 : 1;
+    const dim3 grid((unsigned)(tiles / nt)), block(kS1Waves * kWave);
     if (dtype == MEDUSA_BF16) {
-        auto *kern = four ? heads_stage1_kernel<bf16_t, 4> : heads_stage1_kernel<bf16_t, 1>;
+        auto *kern = nt == 4 ? heads_stage1_kernel<bf16_t, 4>
+                   : nt == 5 ? heads_stage1_kernel<bf16_t, 5> : heads_stage1_kernel<bf16_t, 1>;
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)hidden, (const bf16_t *)w1,
                            (bf16_t *)(base + L.z_off), B, K, d);
     } else {
-        auto *kern = four ? heads_stage1_kernel<float, 4> : heads_stage1_kernel<float, 1>;
+        auto *kern = nt == 4 ? heads_stage1_kernel<float, 4>
+                   : nt == 5 ? heads_stage1_kernel<float, 5> : heads_stage1_kernel<float, 1>;
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)hidden, (const float *)w1,
                            (float *)(base + L.z_off), B, K, d);
     }

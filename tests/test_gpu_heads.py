@@ -64,6 +64,17 @@ def test_heads_four_tile_stage1_partial_batch():
     assert amb <= 1
 
 
+def test_heads_five_tile_stage1_across_heads():
+    # K = 5 heads of 4096 rows: stage 1 runs 256 workgroups of five tiles,
+    # and the groups that straddle a head boundary write into two heads
+    B, K, d, V, s = 5, 5, 4096, 300, 3
+    hx = _random_heads(5151, B, K, d, V, "bf16")
+    out = _run(hx, s, "bf16")
+    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "bf16")
+    amb = _compare(out, ref, s, "bf16")
+    assert amb <= 1
+
+
 def test_heads_exact_small_integers():
     """Values on a coarse binary grid make every fp32 sum exact: logits must be
     bit-identical to the oracle's."""
