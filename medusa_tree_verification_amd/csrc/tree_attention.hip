@@ -7,8 +7,10 @@
 // Work decomposition.  For a (sequence b, kv head) pair, the G = Hq/Hkv
 // query heads that share it and the T tree nodes form M = G*T query rows that
 // all read the same keys, so they are packed as the N dimension of one MFMA
-// problem and share every K/V tile staged in LDS.  A workgroup of W <= 8
-// waves owns 32*W rows (an "m-tile") and one slice ("split") of the prefix;
+// problem and share every K/V tile staged in LDS.  A workgroup of eight
+// waves owns 32*W rows (an "m-tile"; W <= 8 row waves, or 2W waves when each
+// row wave takes one 32-key half of every stage) and one slice ("split") of
+// the prefix; the other waves only stage K/V;
 // the split holding the end of the prefix also takes the T tree keys, with
 // the ancestor-or-self mask applied from per-row bitmasks that each lane
 // builds from the parent array (kernel argument).  Splits are merged by a
