@@ -64,6 +64,15 @@ def test_heads_four_tile_stage1_partial_batch():
     assert amb <= 1
 
 
+def test_heads_four_tile_stage1_f32():
+    B, K, d, V, s = 4, 4, 4096, 200, 3
+    hx = _random_heads(4343, B, K, d, V, "f32")
+    out = _run(hx, s, "f32")
+    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "f32")
+    amb = _compare(out, ref, s, "f32")
+    assert amb <= 1
+
+
 def test_heads_five_tile_stage1_across_heads():
     # K = 5 heads of 4096 rows: stage 1 runs 256 workgroups of five tiles,
     # and the groups that straddle a head boundary write into two heads
