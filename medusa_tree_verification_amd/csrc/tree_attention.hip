@@ -405,9 +405,10 @@ __global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_ke
     // PD stages earlier) is written to buffer (i+1)%2, free since the last
     // barrier, the loads of stage i+1+PD go out into the register set it
     // freed, and stage i is computed from buffer i%2.  Staging first lets the
-    // waves without V units start computing while the others transpose V.  The loop is unrolled by PD so that every
-    // register set is named statically; it runs a multiple of PD stages, the
-    // ones past the last computing nothing.
+    // waves without V units start computing while the others transpose V.
+    // The loop is unrolled by PD so that every register set is named
+    // statically; it runs a multiple of PD stages, the ones past the last
+    // computing nothing.
     // prologue: stages 0 .. PD-1 in flight, stage 0 to LDS, stage PD issued
 #pragma unroll
     for (int k = 0; k < PD; ++k) issue(cp[k], k);
