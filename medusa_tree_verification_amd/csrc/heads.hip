@@ -10,9 +10,12 @@
 // the (at most 16) batch columns, so one kernel serves every B <= 16 and the
 // FLOPs cost nothing next to the bytes.
 //
-// Stage 1: grid of 16-row tiles over the K*d rows of W1, four waves per tile
-//   splitting the d reduction; LDS sum; epilogue z = SiLU(u) + h written to
-//   the workspace (bf16 rounding once, in bf16 mode).
+// Stage 1: the 16-row tiles over the K*d rows of W1, one per workgroup, or
+//   four or five consecutive ones from four sequences on when such groups
+//   fill the CUs evenly (the hidden-state loads are then shared by the
+//   tiles); four waves split the d reduction; LDS sum; epilogue
+//   z = SiLU(u) + h written to the workspace (bf16 rounding once, in bf16
+//   mode).
 // Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over one
 //   workgroup of four waves per CU (measured: more concurrent waves streaming
 //   16-row tiles lose HBM efficiency).  Each wave streams up to four tiles at
