@@ -190,3 +190,15 @@ def test_stage2_split_validation(mv):
     assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 9, 1, FAKE, None, FAKE_WS, 1 << 40, None) == -2
     assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 3, 7, FAKE, None, FAKE_WS, 1 << 40, None) == -3
     assert L.medusa_heads_stage2_merge(1, 4, 4096, 32000, 3, 1, FAKE, None, None, 1 << 40, None) == -5
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark runs on one GPU; asking for more exits with a message
+    before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
