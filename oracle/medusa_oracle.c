@@ -298,14 +298,19 @@ int oracle_tree_attention(const void *q, const void *k_cache, const void *v_cach
             sc[k] = exp(sc[k] - m);
             den += sc[k];
         }
-        for (int e = 0; e < dh; ++e) {
-            double acc = 0.0;
-            for (int p = 0; p < L; ++p)
-                acc += sc[p] * ld(v_cache, coff + (size_t)p * dh + e, dtype);
-            for (int a = 0; a < na; ++a)
-                acc += sc[L + a] * ld(v_tree, toff + (size_t)anc[a] * dh + e, dtype);
-            o[e] = acc / den;
-        }
+        /* o[e] = sum over the visible keys in the order prefix 0..L-1, then
+           the ancestors; the key loop is outside so that each V row is read
+           once (each o[e] still sums its terms in that same order) */
+        for (int e = 0; e < dh; ++e)
+            o[e] = 0.0;
+        for (int p = 0; p < L; ++p)
+            for (int e = 0; e < dh; ++e)
+                o[e] += sc[p] * ld(v_cache, coff + (size_t)p * dh + e, dtype);
+        for (int a = 0; a < na; ++a)
+            for (int e = 0; e < dh; ++e)
+                o[e] += sc[L + a] * ld(v_tree, toff + (size_t)anc[a] * dh + e, dtype);
+        for (int e = 0; e < dh; ++e)
+            o[e] /= den;
         free(sc);
         free(anc);
     }
