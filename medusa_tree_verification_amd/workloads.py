@@ -37,6 +37,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 CHUNK = 1 << 22  # elements per independently seeded chunk
+# A re-drawn sequence row (hidden state) or re-planted logits row uses the
+# stream's seed plus k * RESEED_STRIDE for its k-th re-draw (k >= 1).
+RESEED_STRIDE = 100000
 
 F32 = "f32"
 BF16 = "bf16"
@@ -272,10 +275,25 @@ def workload_tree(wl: Workload) -> Tree:
 # --------------------------------------------------------------------------
 # per-stage inputs
 # --------------------------------------------------------------------------
-def heads_inputs(wl: Workload) -> Dict[str, np.ndarray]:
+def redrawn_row(seed: int, row: int, k: int, n: int, std: float, dtype: str) -> np.ndarray:
+    """Row `row` of a tensor drawn from stream `seed`, re-drawn for the k-th
+    time (k >= 1): N(0, std^2) from SeedSequence([seed + k*RESEED_STRIDE, row])."""
+    a = _rng(seed + k * RESEED_STRIDE, row).standard_normal(n, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return encode(a, dtype)
+
+
+def heads_inputs(wl: Workload, reseed: Optional[Dict[int, int]] = None) -> Dict[str, np.ndarray]:
+    """hidden, W1, W2 of the workload.  reseed maps a sequence b to its
+    re-draw count k: hidden[b] then comes from redrawn_row(stream 1, b, k)."""
     base = 1000 * wl.cid
+    hidden = normal_tensor(base + 1, (wl.B, wl.d), 1.0, wl.dtype)
+    for b, k in sorted((reseed or {}).items()):
+        if k > 0:
+            hidden[b] = redrawn_row(base + 1, b, k, wl.d, 1.0, wl.dtype)
     return {
-        "hidden": normal_tensor(base + 1, (wl.B, wl.d), 1.0, wl.dtype),
+        "hidden": hidden,
         "w1": normal_tensor(base + 2, (wl.K, wl.d, wl.d), 0.02, wl.dtype),
         "w2": normal_tensor(base + 3, (wl.K, wl.V, wl.d), 0.02, wl.dtype),
     }
@@ -323,8 +341,71 @@ def path_tokens(tree: Tree, table: np.ndarray) -> np.ndarray:
     return out
 
 
-def verify_logits(wl: Workload, tree: Tree, tokens: np.ndarray,
+def _children(tree: Tree) -> Dict[int, List[int]]:
+    kids: Dict[int, List[int]] = {}
+    for n in range(1, tree.T):
+        kids.setdefault(int(tree.parent[n]), []).append(n)
+    return kids
+
+
+def _plant_row(wl: Workload, tree: Tree, row: np.ndarray, n: int, ch: List[int],
+               child_tok: List[int], rng: np.random.Generator) -> None:
+    """Plant the children of internal node n into its fp32 noise row (in place)."""
+    V = wl.V
+    depth = len(tree.paths[n])
+    a = float(wl.rates[min(depth, len(wl.rates) - 1)])
+    ranks = [tree.paths[c][-1] for c in ch]
+    if wl.mode == "greedy":
+        probs = [a * (1 - a) ** r for r in ranks]
+        u = rng.random()
+        pick = -1
+        acc = 0.0
+        for i, p in enumerate(probs):
+            acc += p
+            if u < acc:
+                pick = i
+                break
+        if pick >= 0:
+            tok = child_tok[pick]
+        else:
+            tok = int(rng.integers(V))
+            while tok in child_tok:
+                tok = int(rng.integers(V))
+        row[tok] = row.max() + rng.uniform(0.5, 1.5)
+    else:
+        peak = rng.uniform(11.0, 14.5)
+        accept = [rng.random() < a * (1 - a) ** r for r in ranks]
+        if accept and accept[0] and ranks[0] == 0:
+            peak_tok = child_tok[0]
+        else:
+            peak_tok = int(rng.integers(V))
+            while peak_tok in child_tok:
+                peak_tok = int(rng.integers(V))
+        row[peak_tok] = peak
+        for i, t in enumerate(child_tok):
+            if accept[i] and t != peak_tok:
+                row[t] = peak - rng.uniform(0.3, 1.5)
+        row *= np.float32(wl.temperature)
+
+
+def replanted_row(wl: Workload, tree: Tree, tokens: np.ndarray, b: int, n: int, k: int,
                   seed_base: Optional[int] = None) -> np.ndarray:
+    """Logits row (b, n) of an internal node n, re-planted for the k-th time
+    (k >= 1): fresh noise and planting draws from streams 10 and 11 at
+    seed + k*RESEED_STRIDE, row index b*T + n.  Returned in stored form."""
+    base = 1000 * wl.cid if seed_base is None else seed_base
+    T = tree.T
+    ch = _children(tree)[n]
+    idx = b * T + n
+    row = _rng(base + 10 + k * RESEED_STRIDE, idx).standard_normal(wl.V, dtype=np.float32)
+    _plant_row(wl, tree, row, n, ch, [int(tokens[b, c]) for c in ch],
+               _rng(base + 11 + k * RESEED_STRIDE, idx))
+    return encode(row, wl.dtype) if wl.dtype == BF16 else row
+
+
+def verify_logits(wl: Workload, tree: Tree, tokens: np.ndarray,
+                  seed_base: Optional[int] = None,
+                  replant: Optional[Dict[Tuple[int, int], int]] = None) -> np.ndarray:
     """Verification logits [B][T][V] with candidates planted to be accepted at
     roughly the per-depth rates (a geometric model over sibling ranks).
 
@@ -336,60 +417,28 @@ def verify_logits(wl: Workload, tree: Tree, tokens: np.ndarray,
       over roughly 0.4-5 nats at V = 32000..128256; children drawn as
       "accept" get a logit U(0.3, 1.5) below the peak (the rank-0 one may
       become the peak itself), the others keep their noise value.
-    Leaf rows are plain noise.
+    Leaf rows are plain noise.  replant maps (b, n) of an internal node to
+    its re-plant count k: that row is then replanted_row(..., k).
     """
     base = 1000 * wl.cid if seed_base is None else seed_base
     B, T, V = wl.B, tree.T, wl.V
     noise = normal_tensor(base + 10, (B, T, V), 1.0, F32)
     rng = _rng(base + 11)
-    kids: Dict[int, List[int]] = {}
-    for n in range(1, T):
-        kids.setdefault(int(tree.parent[n]), []).append(n)
+    kids = _children(tree)
     tau = float(wl.temperature)
     for b in range(B):
         for n, ch in kids.items():
-            row = noise[b, n]
-            depth = len(tree.paths[n])
-            a = float(wl.rates[min(depth, len(wl.rates) - 1)])
-            child_tok = [int(tokens[b, c]) for c in ch]
-            ranks = [tree.paths[c][-1] for c in ch]
-            if wl.mode == "greedy":
-                probs = [a * (1 - a) ** r for r in ranks]
-                u = rng.random()
-                pick = -1
-                acc = 0.0
-                for i, p in enumerate(probs):
-                    acc += p
-                    if u < acc:
-                        pick = i
-                        break
-                if pick >= 0:
-                    tok = child_tok[pick]
-                else:
-                    tok = int(rng.integers(V))
-                    while tok in child_tok:
-                        tok = int(rng.integers(V))
-                row[tok] = row.max() + rng.uniform(0.5, 1.5)
-            else:
-                peak = rng.uniform(11.0, 14.5)
-                accept = [rng.random() < a * (1 - a) ** r for r in ranks]
-                if accept and accept[0] and ranks[0] == 0:
-                    peak_tok = child_tok[0]
-                else:
-                    peak_tok = int(rng.integers(V))
-                    while peak_tok in child_tok:
-                        peak_tok = int(rng.integers(V))
-                row[peak_tok] = peak
-                for i, t in enumerate(child_tok):
-                    if accept[i] and t != peak_tok:
-                        row[t] = peak - rng.uniform(0.3, 1.5)
-                row *= np.float32(tau)
+            _plant_row(wl, tree, noise[b, n], n, ch, [int(tokens[b, c]) for c in ch], rng)
         if wl.mode == "typical":
             # leaf rows: same tempered scale as the internal ones
             for n in range(T):
                 if n not in kids:
                     noise[b, n] *= np.float32(tau)
-    return encode(noise, wl.dtype) if wl.dtype == BF16 else noise
+    out = encode(noise, wl.dtype) if wl.dtype == BF16 else noise
+    for (b, n), k in sorted((replant or {}).items()):
+        if k > 0:
+            out[b, n] = replanted_row(wl, tree, tokens, b, n, k, base)
+    return out
 
 
 def forward_inputs(wl: Workload, N: int, T: Optional[int] = None,

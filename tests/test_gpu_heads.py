@@ -1,10 +1,14 @@
-"""GPU parity: medusa_heads_topk against the CPU oracle (through the C ABI)."""
+"""GPU parity: medusa_heads_topk against the CPU oracle (through the C ABI).
+
+Inputs pass the G1 guard (tests/guards.py), so the top-s ids and the root
+token have one right answer and are compared exactly."""
 import numpy as np
 import pytest
 
 import oracle
 from medusa_tree_verification_amd import workloads as W
-from tests.util import from_dev, normwise, to_dev, topk_check
+from tests import guards
+from tests.util import Canaries, normwise, to_dev, topk_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -12,27 +16,42 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
 def _run(hx, s, dtype, **kw):
+    import torch
     from medusa_tree_verification_amd import binding as mv
-    out = mv.medusa_heads_topk(to_dev(hx["hidden"]), to_dev(hx["w1"]), to_dev(hx["w2"]), s,
-                               want_logits=True, **kw)
+    B, d = hx["hidden"].shape
+    K, V = hx["w2"].shape[0], hx["w2"].shape[1]
+    cz = Canaries()
+    out = {"topk_ids": cz.empty((B, K, s), torch.int32),
+           "topk_vals": cz.empty((B, K, s), torch.float32),
+           "logits": cz.empty((B, K, V), torch.float32)}
+    mv.medusa_heads_topk(to_dev(hx["hidden"]), to_dev(hx["w1"]), to_dev(hx["w2"]), s, out=out,
+                         **kw)
+    cz.check()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def _compare(out, ref, s, dtype):
+def _compare(out, ref, s, dtype, label=""):
     err = normwise(out["logits"], ref["logits"], axes=2)
     assert err.max() < TOL[dtype], err.max()
-    amb = topk_check(out["topk_ids"], ref["logits"], ref["topk_ids"], s, out["logits"])
+    topk_exact(out["topk_ids"], ref["topk_ids"], ref["logits"], s, out["logits"], label)
     # values reported with the ids are the logits of those ids
-    B, K, _ = ref["logits"].shape
     vals_ref = np.take_along_axis(ref["logits"], out["topk_ids"].astype(np.int64), axis=2)
     assert normwise(out["topk_vals"], vals_ref, axes=(1, 2)).max() < TOL[dtype]
-    return amb
 
 
-def _random_heads(seed, B, K, d, V, dtype, wstd=0.05):
-    return {"hidden": W.normal_tensor(seed + 1, (B, d), 1.0, dtype),
-            "w1": W.normal_tensor(seed + 2, (K, d, d), wstd, dtype),
-            "w2": W.normal_tensor(seed + 3, (K, V, d), wstd, dtype)}
+def _random_heads(seed, B, K, d, V, dtype, wstd=0.05, s=None, w_lm_std=None):
+    """Random heads inputs (hidden ~ N(0,1), weights ~ N(0, wstd^2)) under G1
+    for top-s (and the LM head when w_lm_std is given).  Returns (hx, ref,
+    lm_ref)."""
+    hx = {"hidden": W.normal_tensor(seed + 1, (B, d), 1.0, dtype),
+          "w1": W.normal_tensor(seed + 2, (K, d, d), wstd, dtype),
+          "w2": W.normal_tensor(seed + 3, (K, V, d), wstd, dtype)}
+    if w_lm_std is not None:
+        hx["w_lm"] = W.normal_tensor(seed + 4, (V, d), w_lm_std, dtype)
+    ref, lm, _ = guards.guard_heads(hx, s, dtype,
+                                    lambda b, k: W.redrawn_row(seed + 1, b, k, d, 1.0, dtype),
+                                    f"random heads seed {seed}", w_lm=hx.get("w_lm"))
+    return hx, ref, lm
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -46,42 +65,31 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05):
     (7, 4, 128, 70000, 3),     # many tiles per workgroup
 ])
 def test_heads_random_shapes(dtype, B, K, d, V, s):
-    hx = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype)
+    hx, ref, _ = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype, s=s)
     out = _run(hx, s, dtype)
-    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, dtype)
-    amb = _compare(out, ref, s, dtype)
-    assert amb <= max(1, B * K // 20)
+    _compare(out, ref, s, dtype, f"random B={B} K={K} d={d} V={V} s={s} {dtype}")
 
 
 def test_heads_four_tile_stage1_partial_batch():
     # K * d / 64 = 256 tile groups and B >= 4: stage 1 gives each workgroup
     # four tiles; 6 of the 16 MFMA columns hold sequences
     B, K, d, V, s = 6, 4, 4096, 300, 3
-    hx = _random_heads(4242, B, K, d, V, "bf16")
-    out = _run(hx, s, "bf16")
-    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "bf16")
-    amb = _compare(out, ref, s, "bf16")
-    assert amb <= 1
+    hx, ref, _ = _random_heads(4242, B, K, d, V, "bf16", s=s)
+    _compare(_run(hx, s, "bf16"), ref, s, "bf16", "four-tile groups, 6 sequences")
 
 
 def test_heads_four_tile_stage1_f32():
     B, K, d, V, s = 4, 4, 4096, 200, 3
-    hx = _random_heads(4343, B, K, d, V, "f32")
-    out = _run(hx, s, "f32")
-    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "f32")
-    amb = _compare(out, ref, s, "f32")
-    assert amb <= 1
+    hx, ref, _ = _random_heads(4343, B, K, d, V, "f32", s=s)
+    _compare(_run(hx, s, "f32"), ref, s, "f32", "four-tile groups, fp32")
 
 
 def test_heads_five_tile_stage1_across_heads():
     # K = 5 heads of 4096 rows: stage 1 runs 256 workgroups of five tiles,
     # and the groups that straddle a head boundary write into two heads
     B, K, d, V, s = 5, 5, 4096, 300, 3
-    hx = _random_heads(5151, B, K, d, V, "bf16")
-    out = _run(hx, s, "bf16")
-    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], s, "bf16")
-    amb = _compare(out, ref, s, "bf16")
-    assert amb <= 1
+    hx, ref, _ = _random_heads(5151, B, K, d, V, "bf16", s=s)
+    _compare(_run(hx, s, "bf16"), ref, s, "bf16", "five-tile groups across heads")
 
 
 def test_heads_exact_small_integers():
@@ -101,19 +109,17 @@ def test_heads_exact_small_integers():
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_heads_workloads(name):
     wl = W.WORKLOADS[name]
-    hx = W.heads_inputs(wl)
+    hx, ref, bumps = guards.workload_heads(name)
+    print(f"{name}: G1 re-drawn sequences {bumps or 'none'}")
     out = _run(hx, wl.s, wl.dtype)
-    ref = oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], wl.s, wl.dtype)
-    amb = _compare(out, ref, wl.s, wl.dtype)
-    print(f"{name}: near-tie top-s rows {amb} of {wl.B * wl.K}")
-    assert amb <= 1
+    _compare(out, ref, wl.s, wl.dtype, name)
 
 
 def test_heads_stages_equal_fused_call_and_repeat_bit_identical():
     from medusa_tree_verification_amd import binding as mv
     import torch
     wl = W.WORKLOADS["llama7b_b1"]
-    hx = _random_heads(777, 5, 4, 512, 5000, "bf16")
+    hx, _, _ = _random_heads(777, 5, 4, 512, 5000, "bf16", s=3)
     h, w1, w2 = (to_dev(hx[k]) for k in ("hidden", "w1", "w2"))
     B, K, d, V, s = 5, 4, 512, 5000, 3
     a = mv.medusa_heads_topk(h, w1, w2, s, want_logits=True)
@@ -146,23 +152,13 @@ def _root_run(hx, s):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def _root_check(out, hx, dtype):
-    """The GPU's root must be the oracle's argmax unless the oracle's top two
-    logits are within the GPU's own logit error (then it must be within that
-    error of the maximum).  Returns the number of such near-tie rows."""
-    ref = oracle.lm_head_argmax(hx["hidden"], hx["w_lm"], dtype)
-    lg = ref["logits"]
-    near = 0
-    for b in range(lg.shape[0]):
-        t = int(out["root_token"][b])
-        band = 4 * max(abs(float(out["root_val"][b]) - lg[b, t]), 1e-6 * np.abs(lg[b]).max())
-        top2 = np.sort(lg[b])[-2:] if lg.shape[1] > 1 else np.array([lg[b, 0], -np.inf])
-        assert lg[b, t] >= top2[-1] - band, (b, t, lg[b, t], top2)
-        if top2[-1] - top2[-2] > band:
-            assert t == ref["token"][b]
-        else:
-            near += 1
-    return near
+def _root_check(out, lm, dtype):
+    """The root token is the oracle's LM-head argmax (exact: G1 keeps the top
+    two logits apart) and root_val its logit to the dtype's tolerance."""
+    np.testing.assert_array_equal(out["root_token"], lm["token"])
+    lg = lm["logits"]
+    val_ref = lg[np.arange(lg.shape[0]), lm["token"]]
+    assert normwise(out["root_val"][None], val_ref[None], axes=1).max() < TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -170,23 +166,22 @@ def _root_check(out, hx, dtype):
                                        (16, 5, 256, 4099, 3), (7, 4, 128, 70000, 3)])
 def test_heads_root_random(dtype, B, K, d, V, s):
     seed = hash((B, K, d, V, s, 7)) % 10000 * 10
-    hx = _random_heads(seed, B, K, d, V, dtype)
-    hx["w_lm"] = W.normal_tensor(seed + 4, (V, d), 0.05, dtype)
+    hx, ref, lm = _random_heads(seed, B, K, d, V, dtype, s=s, w_lm_std=0.05)
     out = _root_run(hx, s)
-    # the Medusa heads' results are those of the plain call (the extra head
-    # moves the work split, hence the order of the k-sums: values agree to
-    # rounding, ids except where two candidates are that close)
+    # the Medusa heads' results are those of the plain call: ids exactly,
+    # values to rounding (the extra head moves the work split, hence the
+    # order of the k-sums)
     plain = _run(hx, s, dtype)
+    np.testing.assert_array_equal(out["topk_ids"], plain["topk_ids"])
+    np.testing.assert_array_equal(out["topk_ids"], ref["topk_ids"])
     np.testing.assert_allclose(out["topk_vals"], plain["topk_vals"], rtol=1e-5, atol=1e-6)
-    diff = out["topk_ids"] != plain["topk_ids"]
-    np.testing.assert_allclose(out["topk_vals"][diff], plain["topk_vals"][diff], rtol=1e-5)
-    assert _root_check(out, hx, dtype) <= max(1, B // 8)
+    _root_check(out, lm, dtype)
 
 
 def test_heads_root_workload_shape():
     """Llama-7B shapes (d 4096, V 32000, bf16) with a planted root per row."""
     wl = W.WORKLOADS["ragged_b16_gqa_typical"]
-    hx = W.heads_inputs(wl)
+    hx = dict(guards.workload_heads(wl.name)[0])
     w_lm = W.normal_tensor(1000 * wl.cid + 20, (wl.V, wl.d), 0.02, wl.dtype)
     h = W.decode(hx["hidden"], wl.dtype)
     rng = np.random.default_rng(21)
@@ -194,6 +189,8 @@ def test_heads_root_workload_shape():
     for b in range(wl.B):
         w_lm[plant[b]] = W.encode(h[b] / np.linalg.norm(h[b]) * 0.5, wl.dtype)
     hx["w_lm"] = w_lm
+    lm = oracle.lm_head_argmax(hx["hidden"], w_lm, wl.dtype)
+    assert all(guards.topk_margin(lm["logits"][b], 2) >= guards.G_REL for b in range(wl.B))
     out = _root_run(hx, wl.s)
-    assert _root_check(out, hx, wl.dtype) == 0
+    _root_check(out, lm, wl.dtype)
     np.testing.assert_array_equal(out["root_token"], plant)
