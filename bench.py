@@ -37,10 +37,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama7b_b1", choices=W.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default="large_vocab_typical", choices=W.WORKLOAD_ORDER,
+                    help="default: the largest workload (K=5 heads, V=128256, batch 8, "
+                         "256-node tree, typical acceptance)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the oracle timing")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB read before each step of the per-call breakdown pass, outside "
@@ -249,6 +251,9 @@ def main():
     dom = "heads_stage2"
     achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
+    attn_bound = stages["tree_attention"]["bound"]
+    attn_tf = flops / (per["tree_attention"] * 1e-3) / 1e12
+    attn_gbs = nbytes["tree_attention"] / (per["tree_attention"] * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 2),
@@ -274,6 +279,17 @@ def main():
         "roofline": {"kernel": "heads_stage2_kernel (medusa_heads_stage2_stream: W2 stream + fused per-workgroup top-s)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "roofline_tree_attention": (
+            {"kernel": "tree_attn_fwd_kernel (+ tree_attn_combine_kernel when the prefix is "
+                       "split): the tree_attention call", "bound": "mfma",
+             "achieved": round(attn_tf, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(attn_tf / PEAK_MFMA_TFLOPS, 4), "hbm_GBps": round(attn_gbs, 1),
+             "flops": int(flops)} if attn_bound == "mfma" else
+            {"kernel": "tree_attn_fwd_kernel (+ tree_attn_combine_kernel when the prefix is "
+                       "split): the tree_attention call", "bound": "hbm",
+             "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(attn_tf, 1),
+             "bytes": int(nbytes["tree_attention"])}),
         "stages": stages,
     }
 
@@ -389,25 +405,56 @@ def measure_forward(mv, wl, tree, plen, plen_np, steps, N):
     return r
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, hx, ax, tree, cand, vlog_np, budget_s):
-    """The oracle, as it stands, on the host cores: full verify steps of the
-    same workload (same input bytes) repeated until the time budget is spent."""
+    """The oracle, as it stands, on the host cores: the time of one verify
+    step of the same workload (same input bytes).  Heads and acceptance run
+    whole; the tree attention runs on an evenly spaced sample of its output
+    rows sized to the time budget, and its time is scaled to all rows."""
     import oracle
-    reps = 0
     t0 = time.perf_counter()
-    while True:
-        oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], wl.s, wl.dtype)
+    oracle.heads_topk(hx["hidden"], hx["w1"], hx["w2"], wl.s, wl.dtype)
+    t_heads = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.tree_accept(vlog_np, cand, tree.parent, wl.dtype, wl.mode, wl.temperature)
+    t_acc = time.perf_counter() - t0
+    nrows = wl.B * wl.Hq * wl.T
+    allrows = np.stack(np.meshgrid(np.arange(wl.B), np.arange(wl.Hq), np.arange(wl.T),
+                                   indexing="ij"), axis=-1).reshape(-1, 3).astype(np.int32)
+
+    def attn(rows):
+        t = time.perf_counter()
         oracle.tree_attention(ax["q"], ax["k_cache"], ax["v_cache"], ax["prefix_len"],
-                              ax["k_tree"], ax["v_tree"], tree.parent, wl.scale, wl.dtype)
-        oracle.tree_accept(vlog_np, cand, tree.parent, wl.dtype, wl.mode, wl.temperature)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
-    return {"value": round(reps / el, 4), "unit": "steps/s", "cores": oracle.num_threads(),
+                              ax["k_tree"], ax["v_tree"], tree.parent, wl.scale, wl.dtype,
+                              rows=rows)
+        return time.perf_counter() - t
+
+    probe = allrows[:: max(1, nrows // 256)]
+    t_probe = attn(probe)
+    left = max(budget_s - t_heads - t_acc - t_probe, 1.0)
+    n = int(min(nrows, max(len(probe), len(probe) * left / max(t_probe, 1e-6))))
+    stride = max(1, nrows // n)
+    sample = allrows[::stride]
+    t_attn = attn(sample) * nrows / len(sample)
+    step_s = t_heads + t_attn + t_acc
+    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{reps} full verify step(s) of {wl.name} (all heads, every attention "
-                      f"row, acceptance) in {el:.1f} s"}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+            "stage_s": {"heads": round(t_heads, 3), "tree_attention": round(t_attn, 3),
+                        "tree_accept": round(t_acc, 3)},
+            "sample": f"one verify step of {wl.name}: heads (all {wl.B} sequences, "
+                      f"{wl.K} heads) and acceptance in full; tree attention on every "
+                      f"{stride}-th of its {nrows} output rows ({len(sample)} rows, "
+                      f"time scaled to all rows)"}
 
 
 if __name__ == "__main__":

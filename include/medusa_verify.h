@@ -29,7 +29,10 @@
  *  - Scratch memory comes from the caller's workspace `ws` of `ws_bytes`
  *    bytes (device, 256-byte aligned), sized by the matching
  *    *_workspace_bytes() call.  Its contents need no initialisation and are
- *    undefined after the call.  Calls that share a workspace must be
+ *    undefined after the call, with one exception: tree_attention leaves
+ *    its prefix-length flag in the workspace's first int32 (see there),
+ *    which every tree_attention call rewrites and any other call on the
+ *    same workspace may overwrite.  Calls that share a workspace must be
  *    ordered on one stream.
  *  - Return value: MEDUSA_OK, or a negative medusa_status.  Argument errors
  *    are detected on the host before anything is enqueued; no output is
@@ -161,7 +164,9 @@ int medusa_heads_topk_root(const void *hidden, const void *w1, const void *w2, c
  *   k_cache     device [B][Hkv][Lcap][dh] dtype
  *   v_cache     device [B][Hkv][Lcap][dh] dtype
  *   prefix_len  device [B] int32; values outside [0, Lcap] are clamped and
- *               flagged in the workspace's first int32 (nonzero = clamped)
+ *               flagged in the workspace's first int32 (nonzero = some value
+ *               was clamped; written by every call, valid until the next
+ *               call on the workspace)
  *   k_tree      device [B][Hkv][T][dh]    dtype (keys of the tree tokens)
  *   v_tree      device [B][Hkv][T][dh]    dtype
  *   parent      host [T] int32: parent[0] = -1, 0 <= parent[n] < n

@@ -32,28 +32,13 @@
 namespace medusa {
 namespace {
 
-#ifndef MEDUSA_S2_TILES
-#define MEDUSA_S2_TILES 4
-#endif
-#ifndef MEDUSA_S2_UNROLL
-#define MEDUSA_S2_UNROLL 8
-#endif
-#ifndef MEDUSA_S2_WG_PER_CU
-#define MEDUSA_S2_WG_PER_CU 1
-#endif
-#ifndef MEDUSA_S2_WAVES
-#define MEDUSA_S2_WAVES 4
-#endif
-#ifndef MEDUSA_S2_BARRIER
-#define MEDUSA_S2_BARRIER 1
-#endif
 constexpr int kSMax = MEDUSA_MAX_TOPS;   // top-s list capacity
 constexpr int kS1Waves = 4;              // stage 1: waves per 16-row tile (split d)
 constexpr int kS1Unroll = 8;             // stage 1: k-steps in flight per wave
-constexpr int kS2Waves = MEDUSA_S2_WAVES;        // stage 2: waves per workgroup
-constexpr int kS2Tiles = MEDUSA_S2_TILES;        // stage 2: row tiles per wave pass
-constexpr int kS2Unroll = MEDUSA_S2_UNROLL;      // stage 2: k-steps per batch of loads
-constexpr int kS2MaxWG = MEDUSA_S2_WG_PER_CU * kNumCU;   // stage 2: workgroups
+constexpr int kS2Waves = 4;              // stage 2: waves per workgroup
+constexpr int kS2Tiles = 4;              // stage 2: row tiles per wave pass
+constexpr int kS2Unroll = 8;             // stage 2: k-steps per batch of loads
+constexpr int kS2MaxWG = kNumCU;         // stage 2: workgroups (one per CU)
 
 struct HeadsLayout {
     size_t z_off, part_off, total;
@@ -261,10 +246,8 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
         for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int u = 0; u < kS2Unroll; ++u) a[r][u] = ld16(arow[r] + k0 + u * KSTEP);
-#if MEDUSA_S2_BARRIER
         // keep the whole batch of loads ahead of the MFMAs: more bytes in flight
         __builtin_amdgcn_sched_barrier(0);
-#endif
 #pragma unroll
         for (int u = 0; u < kS2Unroll; ++u)
 #pragma unroll
@@ -353,10 +336,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
     int tile = (int)(wg_beg + span * wv / kS2Waves);
     const int wend = (int)(wg_beg + span * (wv + 1) / kS2Waves);
-#ifndef MEDUSA_S2_ROT
-#define MEDUSA_S2_ROT 1
-#endif
-    const int rot = MEDUSA_S2_ROT ? (int)(((unsigned)wg * kS2Waves + wv) * 7u) : 0;
+    const int rot = (int)(((unsigned)wg * kS2Waves + wv) * 7u);
     __syncthreads();
 
     const bool bcol = c < B;

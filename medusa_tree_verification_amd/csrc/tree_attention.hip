@@ -30,27 +30,12 @@
 namespace medusa {
 namespace {
 
-#ifndef MEDUSA_ATTN_MIN_CHUNK
-#define MEDUSA_ATTN_MIN_CHUNK 384
-#endif
-#ifndef MEDUSA_ATTN_WG_PER_CU
-#define MEDUSA_ATTN_WG_PER_CU 1
-#endif
 constexpr int kBN = 64;          // keys per LDS stage
 constexpr int kMaxWaves = 8;     // waves per workgroup
-#ifndef MEDUSA_ATTN_MINWG
-#define MEDUSA_ATTN_MINWG 1      // the launch targets one workgroup per CU
-#endif
-#ifndef MEDUSA_ATTN_PD
-#define MEDUSA_ATTN_PD 2
-#endif
-constexpr int kPD = MEDUSA_ATTN_PD;   // stages of K/V loads in flight (bf16; fp32: 1)
-// Depths 1-3 pass the parity tests; depth 4 with eight waves per workgroup
-// gave run-to-run different results in them (cause not found), so it is
-// not allowed.
-static_assert(kPD >= 1 && kPD <= 3, "prefetch depth 1..3");
-constexpr int kMinChunk = MEDUSA_ATTN_MIN_CHUNK;   // smallest prefix split (keys)
-constexpr int kTargetWG = MEDUSA_ATTN_WG_PER_CU * kNumCU;
+// Stages of K/V loads in flight (bf16; fp32 stages are twice as large: 1).
+constexpr int kPD = 2;
+constexpr int kMinChunk = 384;   // smallest prefix split (keys)
+constexpr int kTargetWG = kNumCU;   // the launch targets one workgroup per CU
 
 template <typename T, int DH>
 struct Cfg {
@@ -276,7 +261,7 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 // rows (with ks = 2, two waves per row tile, one per 32-key half of each
 // stage), all of them share the staging of K/V.
 template <typename T, int DH, int NW>
-__global__ __launch_bounds__(NW *kWave, MEDUSA_ATTN_MINWG) void tree_attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams p) {
     using C = Cfg<T, DH>;
     constexpr int NT = NW * kWave;
     __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
