@@ -37,8 +37,10 @@
  *  - Return value: MEDUSA_OK, or a negative medusa_status.  Argument errors
  *    are detected on the host before anything is enqueued; no output is
  *    touched then.  MEDUSA_ERR_LAUNCH reports a failed kernel launch.
- *  - The library holds no global state and is safe to call from several
- *    host threads (on different workspaces).
+ *  - The library is safe to call from several host threads (on different
+ *    workspaces).  Its only global state is the scratch array of
+ *    medusa_heads_topk_noalloc (one per GPU) and that array's per-device
+ *    address, looked up under a lock on the first such call on a device.
  */
 #ifndef MEDUSA_VERIFY_H
 #define MEDUSA_VERIFY_H
@@ -66,7 +68,8 @@ typedef enum {
     MEDUSA_ERR_TREE = -4,      /* parent / node_rank array is not a valid tree */
     MEDUSA_ERR_WORKSPACE = -5, /* workspace missing, misaligned or too small */
     MEDUSA_ERR_PARAM = -6,     /* bad scalar (mode, temperature, eps, delta, scale) */
-    MEDUSA_ERR_LAUNCH = -7     /* a kernel launch failed                  */
+    MEDUSA_ERR_LAUNCH = -7,    /* a kernel launch failed                  */
+    MEDUSA_ERR_SCRATCH = -8    /* needs more than the no-allocation entry point's scratch */
 } medusa_status;
 
 /* Supported ranges (checked on the host). */
@@ -127,6 +130,27 @@ int medusa_heads_stage2_merge(int B, int K, int d, int V, int s, int dtype, int3
                               float *topk_vals, void *ws, size_t ws_bytes, void *stream);
 
 size_t medusa_heads_topk_workspace_bytes(int B, int K, int d, int V, int s, int dtype);
+
+/* medusa_heads_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It allocates nothing: its
+ * scratch (z and the per-workgroup top-s lists, the same bytes
+ * medusa_heads_topk_workspace_bytes counts) lives in a static device array
+ * of medusa_heads_topk_noalloc_max_scratch() bytes (8 MiB) that each GPU the
+ * library runs on holds until the process ends.  A problem whose workspace
+ * would exceed it is rejected with MEDUSA_ERR_SCRATCH before anything is
+ * enqueued (every shape with B <= 16, K <= 8 and d <= 4096 fits).
+ * Arguments, limits, results and kernels are those of medusa_heads_topk;
+ * the scratch needs no initialisation (every byte read is first written
+ * by the same call).  All calls on one GPU share its array: calls that
+ * overlap on one GPU (on different streams, or from several host threads
+ * without ordering) race and give undefined results; order them on one
+ * stream.  The first call on a device looks up the array's device address
+ * (MEDUSA_ERR_LAUNCH if that fails). */
+int medusa_heads_topk_noalloc(const void *hidden, const void *w1, const void *w2, int B, int K,
+                              int d, int V, int s, int dtype, float *logits_out,
+                              int32_t *topk_ids, float *topk_vals, void *stream);
+size_t medusa_heads_topk_noalloc_max_scratch(void);
 
 /* medusa_heads_topk plus the tree's root token: the base model's own next
  * token, the argmax of its LM head w_lm on the same hidden state (paper

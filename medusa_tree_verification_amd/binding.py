@@ -23,11 +23,12 @@ GREEDY, TYPICAL, TYPICAL_LOGLIK = 0, 1, 2
 
 STATUS = {0: "MEDUSA_OK", -1: "MEDUSA_ERR_NULL", -2: "MEDUSA_ERR_SHAPE", -3: "MEDUSA_ERR_DTYPE",
           -4: "MEDUSA_ERR_TREE", -5: "MEDUSA_ERR_WORKSPACE", -6: "MEDUSA_ERR_PARAM",
-          -7: "MEDUSA_ERR_LAUNCH"}
+          -7: "MEDUSA_ERR_LAUNCH", -8: "MEDUSA_ERR_SCRATCH"}
 
 EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
            "medusa_heads_stage2", "medusa_heads_stage2_stream", "medusa_heads_stage2_merge",
-           "medusa_heads_topk_workspace_bytes", "tree_attention", "tree_attention_workspace_bytes",
+           "medusa_heads_topk_workspace_bytes", "medusa_heads_topk_noalloc",
+           "medusa_heads_topk_noalloc_max_scratch", "tree_attention", "tree_attention_workspace_bytes",
            "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
            "medusa_verify_forward", "medusa_verify_forward_workspace_bytes", "medusa_status_str",
            "medusa_abi_version"]
@@ -53,6 +54,9 @@ def _load() -> ctypes.CDLL:
     L.medusa_heads_stage2_merge.argtypes = [I, I, I, I, I, I, P, P, P, Z, P]
     L.medusa_heads_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.medusa_heads_topk_workspace_bytes.restype = Z
+    L.medusa_heads_topk_noalloc.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
+    L.medusa_heads_topk_noalloc_max_scratch.argtypes = []
+    L.medusa_heads_topk_noalloc_max_scratch.restype = Z
     L.tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, Z, P]
     L.tree_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.tree_attention_workspace_bytes.restype = Z
@@ -69,7 +73,8 @@ def _load() -> ctypes.CDLL:
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
-    for f in ("medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
+    for f in ("medusa_heads_topk", "medusa_heads_topk_noalloc", "medusa_heads_topk_root",
+              "medusa_heads_stage1",
               "medusa_heads_stage2", "medusa_heads_stage2_stream", "medusa_heads_stage2_merge",
               "tree_attention",
               "tree_accept", "tree_commit_kv", "medusa_sample_token", "medusa_verify_forward"):
@@ -146,6 +151,24 @@ def medusa_heads_topk(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, 
                                _ptr(out.get("logits")), _ptr(out["topk_ids"]),
                                _ptr(out.get("topk_vals")), _ptr(ws), ws.numel(), _stream(stream))
     _check("medusa_heads_topk", rc)
+    return out
+
+
+def medusa_heads_topk_noalloc(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, s: int,
+                              *, out: Dict[str, torch.Tensor],
+                              stream=None) -> Dict[str, torch.Tensor]:
+    """medusa_heads_topk with the library's static scratch instead of a
+    workspace; the caller passes every output (out: topk_ids, and optionally
+    topk_vals and logits), so this wrapper allocates nothing either."""
+    for t, n in ((hidden, "hidden"), (w1, "w1"), (w2, "w2")):
+        _need(t, n)
+    B, d = hidden.shape
+    K, V = w2.shape[0], w2.shape[1]
+    rc = lib.medusa_heads_topk_noalloc(_ptr(hidden), _ptr(w1), _ptr(w2), B, K, d, V, s,
+                                       _dtype_code(hidden), _ptr(out.get("logits")),
+                                       _ptr(out["topk_ids"]), _ptr(out.get("topk_vals")),
+                                       _stream(stream))
+    _check("medusa_heads_topk_noalloc", rc)
     return out
 
 

@@ -29,6 +29,8 @@
 //   head merge them, whose device-scope fences cost more than a launch.
 #include "common.h"
 
+#include <mutex>
+
 namespace medusa {
 namespace {
 
@@ -645,4 +647,55 @@ extern "C" int medusa_heads_topk_root(const void *hidden, const void *w1, const 
     if (st != MEDUSA_OK) return st;
     return launch_stage2(w2, w_lm, hidden, B, K, d, V, s, dtype, logits_out, topk_ids, topk_vals,
                          root_token, root_val, ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// medusa_heads_topk_noalloc: medusa_heads_topk with its scratch (z and the
+// per-workgroup top-s lists) in a file-scope device array instead of a
+// caller workspace, for callers that cannot allocate.  Each GPU the library
+// runs on holds its own copy of the array until the process ends; its
+// device address is looked up once per device (with that device current)
+// and kept, since the array's name in host code is not a device address.
+// ---------------------------------------------------------------------------
+namespace medusa {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of scratch, or nullptr when it cannot be found.
+void *scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace medusa
+
+extern "C" size_t medusa_heads_topk_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+extern "C" int medusa_heads_topk_noalloc(const void *hidden, const void *w1, const void *w2, int B,
+                                         int K, int d, int V, int s, int dtype, float *logits_out,
+                                         int32_t *topk_ids, float *topk_vals, void *stream) {
+    int st = check_heads_args(w2, B, K, d, V, s, dtype);
+    if (st != MEDUSA_OK) return st;
+    if (!hidden || !w1 || !topk_ids) return MEDUSA_ERR_NULL;
+    if (heads_layout(B, K, d, V, dtype).total > kNoAllocScratchBytes) return MEDUSA_ERR_SCRATCH;
+    void *ws = scratch_for_current_device();
+    if (!ws) return MEDUSA_ERR_LAUNCH;
+    st = launch_stage1(hidden, w1, B, K, d, V, dtype, ws, (hipStream_t)stream);
+    if (st != MEDUSA_OK) return st;
+    return launch_stage2(w2, nullptr, nullptr, B, K, d, V, s, dtype, logits_out, topk_ids,
+                         topk_vals, nullptr, nullptr, ws, (hipStream_t)stream);
 }

@@ -768,6 +768,8 @@ extern "C" const char *medusa_status_str(int status) {
         case MEDUSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case MEDUSA_ERR_PARAM: return "bad scalar parameter";
         case MEDUSA_ERR_LAUNCH: return "kernel launch failed";
+        case MEDUSA_ERR_SCRATCH:
+            return "the problem needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(mv):
 
 def test_status_strings_and_version(mv):
     assert mv.lib.medusa_abi_version() == 1
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert mv.status_str(code) and mv.status_str(code) != "unknown status"
     assert mv.status_str(5) == "unknown status"
 
@@ -202,3 +202,23 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_heads_noalloc_validation(mv):
+    """The no-allocation heads call checks its arguments like medusa_heads_topk
+    and rejects problems larger than its static scratch, all on the host."""
+    L = mv.lib
+    cap = L.medusa_heads_topk_noalloc_max_scratch()
+    assert cap == 8 << 20
+
+    def call(hidden=FAKE, w1=FAKE, w2=FAKE, ids=FAKE, B=1, K=4, d=4096, V=32000, s=3, dt=1):
+        return L.medusa_heads_topk_noalloc(hidden, w1, w2, B, K, d, V, s, dt, None, ids, None,
+                                           None)
+    assert call(hidden=None) == -1 and call(ids=None) == -1
+    assert call(dt=5) == -3 and call(B=17) == -2 and call(s=9) == -2
+    # fp32, 16 sequences, 16 heads of 16384: z alone is 16 MiB
+    assert L.medusa_heads_topk_workspace_bytes(16, 16, 16384, 1000, 3, 0) > cap
+    assert call(B=16, K=16, d=16384, V=1000, dt=0) == -8
+    assert "scratch" in mv.status_str(-8)
+    # the largest workload's heads fit
+    assert L.medusa_heads_topk_workspace_bytes(8, 5, 4096, 128256, 3, 1) <= cap
