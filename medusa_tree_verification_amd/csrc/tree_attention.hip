@@ -161,99 +161,164 @@ struct StageCopy {
 };
 
 struct RowState {
-    float m;      // running max of scores * c (log2 units), shared by lane pair
+    float m;      // reference max (log2 units) the block scores are taken
+                  // against; -inf before the first key; shared by the lane pair
     float l;      // this lane's part of the softmax denominator
+    f32x16 negr;  // -m in every element (0 while m = -inf): the accumulator
+                  // each block's first q.k product starts from
 };
 
-// P^T (16 probabilities of one 32-key block, this lane's query) times V^T of
-// those keys, accumulated into O^T.
-template <typename T, int DH>
-__device__ __forceinline__ void pv_block(const char *Vt, const float (&p)[16],
-                                         f32x16 (&o)[Cfg<T, DH>::NDT], int sub, int h, int col) {
-    using C = Cfg<T, DH>;
+// max over lanes l and l ^ 32 (v_permlane32_swap trades the upper half of
+// one operand with the lower half of the other; with both operands x each
+// lane then holds x[l] and x[l ^ 32])
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The first k-step of a 32x32 product, accumulating onto c (not in place).
+__device__ __forceinline__ f32x16 mma32_first(const f32x16 &c, const u32x4 &a, const u32x4 &b, bf16_t) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32_first(const f32x16 &c, const u32x4 &a, const u32x4 &b, float) {
+    f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c,
+                                                      0, 0, 0);
+#pragma unroll
+    for (int e = 1; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc,
+                                                   0, 0, 0);
+    return acc;
+}
+
+// P^T (the probabilities of one 32-key block, this lane's query) times V^T
+// of those keys, accumulated into O^T.  bf16: pk holds them packed in the
+// B-operand order of the two 16-key k-steps; fp32: p[16].
+template <int DH>
+__device__ __forceinline__ void pv_block_bf16(const char *Vt, const u32x4 (&pk)[2],
+                                              f32x16 (&o)[Cfg<bf16_t, DH>::NDT], int sub, int h,
+                                              int col) {
+    using C = Cfg<bf16_t, DH>;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
         const char *vrow = Vt + (dt * 32 + col) * C::VT_STRIDE;
-        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 16 * mm + 8 * h) * 2);
-                u32x4 b;
+        for (int mm = 0; mm < 2; ++mm) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 16 * mm + 8 * h) * 2);
+            mma32_step(o[dt], a, pk[mm], bf16_t{});
+        }
+    }
+}
+template <int DH>
+__device__ __forceinline__ void pv_block_f32(const char *Vt, const float (&p)[16],
+                                             f32x16 (&o)[Cfg<float, DH>::NDT], int sub, int h,
+                                             int col) {
+    using C = Cfg<float, DH>;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) b[w] = pack_bf16x2(p[8 * mm + 2 * w], p[8 * mm + 2 * w + 1]);
-                mma32_step(o[dt], a, b, T{});
-            }
-        } else {
+    for (int dt = 0; dt < C::NDT; ++dt) {
+        const char *vrow = Vt + (dt * 32 + col) * C::VT_STRIDE;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 8 * i + 4 * h) * 4);
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(vrow + (sub * 32 + 8 * i + 4 * h) * 4);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mma32_f32_single(o[dt], __uint_as_float(a[j]), p[4 * i + j]);
-            }
+            for (int j = 0; j < 4; ++j) mma32_f32_single(o[dt], __uint_as_float(a[j]), p[4 * i + j]);
         }
     }
 }
 
 // One 64-key stage for one wave (lane: query column col, keys of half h), as
-// two 32-key blocks: S^T = K Q^T on the matrix cores, running-max update,
-// P^T V^T.  masked: apply kind 0 (key < klim) or kind 1 (tree ancestor bits
-// of mword); full prefix stages skip masking.
+// two 32-key blocks: S^T = K Q^T on the matrix cores, reference update,
+// P^T V^T.  Q is pre-scaled by scale * log2(e) and the first product of a
+// block accumulates onto -m, so the scores leave the matrix cores already
+// in the exponent's frame: p = exp2(s).  masked: apply kind 0 (key < klim)
+// or kind 1 (tree ancestor bits of mword); full prefix stages skip masking.
 template <typename T, int DH>
 __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[Cfg<T, DH>::NKS],
                                              f32x16 (&o)[Cfg<T, DH>::NDT], RowState &st, int lane,
                                              bool masked, int kind, int klim, uint64_t mword,
-                                             float c, int sub_lo, int sub_hi) {
+                                             int sub_lo, int sub_hi) {
     using C = Cfg<T, DH>;
     const char *Ks = lds;
     const char *Vt = lds + C::KS_BYTES;
     const int h = lane >> 5, col = lane & 31;
 #pragma unroll 1
     for (int sub = sub_lo; sub < sub_hi; ++sub) {   // 32-key halves of the stage
-        f32x16 s = {};
         const char *krow = Ks + (sub * 32 + col) * C::KS_STRIDE + h * 16;
+        f32x16 s = mma32_first(st.negr, *reinterpret_cast<const u32x4 *>(krow), qf[0], T{});
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
+        for (int ks = 1; ks < C::NKS; ++ks) {
             const u32x4 a = *reinterpret_cast<const u32x4 *>(krow + ks * 32);
             mma32_step(s, a, qf[ks], T{});
         }
-        // s[r]: key sub*32 + 8*(r/4) + 4h + r%4 of this stage
+        // s[r]: key sub*32 + 4h + 8*(r/4) + r%4 of this stage; after one
+        // shift by sub*32 + 4h each test uses a constant bit position
         if (masked) {
+            const int base = sub * 32 + 4 * h;
+            if (kind == 0) {
+                const int lim = klim - base;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool ok = kind == 0 ? key < klim : ((mword >> key) & 1ull) != 0ull;
-                s[r] = ok ? s[r] : -INFINITY;
+                for (int r = 0; r < 16; ++r)
+                    s[r] = 8 * (r >> 2) + (r & 3) < lim ? s[r] : -INFINITY;
+            } else {
+                const uint32_t bits = (uint32_t)(mword >> base);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[r] = (bits >> (8 * (r >> 2) + (r & 3))) & 1u ? s[r] : -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        float mx = s[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;   // c > 0; log2 units
-        // Lazy rescaling: the reference max only moves when the block max
-        // exceeds it by more than 8 (log2 units), so p <= 2^8 and most blocks
-        // skip the O rescale; the branch is taken by the whole wave or not at
-        // all.  The result does not depend on the reference (exact algebra).
-        const bool need = mx > st.m + 8.0f;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = pair_max(mx);   // relative to the reference
+        // Lazy reference: it only moves when the block max exceeds it by
+        // more than 8 (log2 units), so p <= 2^8 and most blocks skip the O
+        // rescale; the branch is taken by the whole wave or not at all.  The
+        // result does not depend on the reference (exact algebra).
+        const bool need = st.m == -INFINITY ? mx > -INFINITY : mx > 8.0f;
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-            const float mnew = need ? mx : st.m;
-            const float alpha = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mnew);
+            const float sh = need ? mx : 0.f;
+            const float alpha = !need ? 1.f : (st.m == -INFINITY ? 0.f : fast_exp2(-sh));
             st.l *= alpha;
-            st.m = mnew;
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) o[dt] *= alpha;
-        }
-        const float nref = st.m == -INFINITY ? 0.f : -st.m;
-        float p[16];
-        float psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = fast_exp2(fmaf(s[r], c, nref));
-            psum += p[r];
+            for (int r = 0; r < 16; ++r) s[r] -= sh;
+            if (need) st.m = (st.m == -INFINITY ? 0.f : st.m) + sh;
+            const float nr = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.negr[r] = nr;
         }
-        st.l += psum;
-        pv_block<T, DH>(Vt, p, o, sub, h, col);
+        if constexpr (sizeof(T) == 2) {
+            // the probabilities packed to bf16 for the P V product; the row
+            // sum takes the same bf16 values (v_dot2 with ones), so the
+            // weights of numerator and denominator are the same numbers
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+            u32x4 pk[2];
+            float acc = st.l;
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t v = pack_bf16x2(fast_exp2(s[8 * mm + 2 * w]),
+                                                   fast_exp2(s[8 * mm + 2 * w + 1]));
+                    pk[mm][w] = v;
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), ones, acc,
+                                                          false);
+                }
+            st.l = acc;
+            pv_block_bf16<DH>(Vt, pk, o, sub, h, col);
+        } else {
+            float p[16];
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = fast_exp2(s[r]);
+                psum += p[r];
+            }
+            st.l += psum;
+            pv_block_f32<DH>(Vt, p, o, sub, h, col);
+        }
     }
 }
 
@@ -344,10 +409,26 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
         if (par[a] == 255) break;   // a is the root
     }
 
+    // Q pre-scaled into the exponent's frame, scale * log2(e) (bf16: rounded
+    // to bf16 once)
+    {
+        const float cs = p.c;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t v = qf[ks][w];
+                if constexpr (sizeof(T) == 2)
+                    qf[ks][w] = pack_bf16x2(__uint_as_float(v << 16) * cs,
+                                            __uint_as_float(v & 0xFFFF0000u) * cs);
+                else
+                    qf[ks][w] = __float_as_uint(__uint_as_float(v) * cs);
+            }
+    }
     f32x16 o[C::NDT];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{};
-    RowState st{-INFINITY, 0.f};
+    RowState st{-INFINITY, 0.f, f32x16{}};
 
     // stages: prefix keys [kbeg, kend) in blocks of kBN, then (last split) the tree keys
     const T *kcb = (const T *)p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
@@ -356,7 +437,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
     const T *vtb = (const T *)p.vt + ((size_t)b * p.Hkv + kvh) * (size_t)p.T * DH;
     const int npre = (kend - kbeg + kBN - 1) / kBN;
     const int ntree = p.T;        // the lambdas below take no reference to p:
-    const float cscale = p.c;     // that would copy the parameter block to scratch
+                                  // that would copy the parameter block to scratch
     const int nstage = npre + (last ? (ntree + kBN - 1) / kBN : 0);
     const bool computes = kgrp < p.ks;
     const int sub_lo = p.ks == 2 ? kgrp : 0, sub_hi = p.ks == 2 ? kgrp + 1 : 2;
@@ -420,7 +501,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
                 }
                 const bool masked = kind == 1 || klim < kBN;
                 attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword,
-                                    cscale, sub_lo, sub_hi);
+                                    sub_lo, sub_hi);
             }
             __syncthreads();
         }
