@@ -68,6 +68,8 @@ struct AcceptParams {
     uint8_t rank[MEDUSA_MAX_TREE];    // sibling rank: index into the depth's top-s list
     uint8_t depth[MEDUSA_MAX_TREE];
     uint32_t internal[MEDUSA_MAX_TREE / 32];  // bit n: node n has children
+    uint8_t rows[MEDUSA_MAX_TREE];    // the nodes whose rows the stats pass reads
+    int nrows;
 };
 
 __device__ __forceinline__ bool has_children(const AcceptParams &p, int n) {
@@ -121,26 +123,27 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
     return r;
 }
 
-// Argmax over 16-byte chunks: the best chunk's maximum, its first element
-// index and raw bits, resolved to an element index once at the end (fewer
-// operations per element than tracking the index of every element).  The
-// first chunk is always taken; later ones only when strictly larger, so on
-// ties the earlier chunk, and within it the earlier element, wins.
+// Argmax over 16-byte chunks: the best chunk's maximum and its first element
+// index; the element index is resolved once at the end by reading that
+// chunk again (an L2 hit), which costs fewer operations per chunk than
+// carrying its bits.  The first chunk is always taken; later ones only when
+// strictly larger, so on ties the earlier chunk, and within it the earlier
+// element, wins.
 struct ChunkArgMax {
     float v;
     int base;      // element index of the chunk's first element; -1: none yet
-    u32x4 bits;
-    __device__ __forceinline__ void add(const u32x4 &c, float cm, int b) {
+    __device__ __forceinline__ void add(float cm, int b) {
         const bool take = base < 0 || cm > v;
         v = take ? cm : v;
         base = take ? b : base;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) bits[w] = take ? c[w] : bits[w];
     }
+    // rs: the buffer resource the chunks were read through, starting at
+    // element lo of the row
     template <typename T>
-    __device__ __forceinline__ void resolve(ArgMax &am) const {
+    __device__ __forceinline__ void resolve(ArgMax &am, __amdgpu_buffer_rsrc_t rs, int lo) const {
         if (base < 0) return;
         constexpr int E = Elem<T>::kPer16B;
+        const u32x4 bits = buf_ld16(rs, (uint32_t)(base - lo) * (uint32_t)sizeof(T));
         int e0 = E - 1;
 #pragma unroll
         for (int e = E - 1; e >= 0; --e) e0 = chunk_elem<T>(bits, e) == v ? e : e0;
@@ -160,7 +163,7 @@ __device__ __forceinline__ void add_chunk_fast(const u32x4 &c, int base, bool ty
     float cm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, x[e]);
-    cam.add(c, cm, base);
+    cam.add(cm, base);
     if (typical) {
         const float cms = cm * zs;   // zs > 0: the maximum of the scaled chunk
         if (cms > st.m) {
@@ -208,7 +211,7 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
     const auto rs = make_rsrc(row + lo, (uint32_t)(hi - lo) * (uint32_t)sizeof(T));
     if ((V % E) == 0 && (lo % E) == 0 && (hi % E) == 0) {
         const int nch = (hi - lo) / E;
-        ChunkArgMax cam{-INFINITY, -1, u32x4{0u, 0u, 0u, 0u}};
+        ChunkArgMax cam{-INFINITY, -1};
         for (int base = (int)threadIdx.x; base < nch; base += U * NT) {
             u32x4 c[U];
 #pragma unroll
@@ -219,7 +222,7 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
                 if (ch < nch) add_chunk_fast<T>(c[u], lo + ch * E, typical, zs, cam, st);
             }
         }
-        cam.resolve<T>(am);
+        cam.resolve<T>(am, rs, lo);
     } else {
         const int n = hi - lo;
         for (int base = (int)threadIdx.x; base < n; base += U * NT) {
@@ -243,9 +246,8 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) 
     __shared__ ArgMax red[kThreads / kWave];
     __shared__ float redS[3][kThreads / kWave];
     static_assert(kThreads >= MEDUSA_MAX_TREE && kFinThreads % MEDUSA_MAX_TREE == 0, "one thread per tree node");
-    const int j = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+    const int j = blockIdx.x, n = p.rows[blockIdx.y], b = blockIdx.z;
     const bool internal = has_children(p, n);
-    if (!internal && !p.leaves) return;
 
     const int lo = j * p.chunk;
     const int hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
@@ -717,10 +719,13 @@ extern "C" int tree_accept(const void *logits, const int32_t *topk_ids, const in
         for (int n = 0; n < T; ++n) nleaf += !((p.internal[n >> 5] >> (n & 31)) & 1u);
         const size_t leaf_bytes = (size_t)B * nleaf * V * (dtype == MEDUSA_BF16 ? 2 : 4);
         p.leaves = T > 1 && leaf_bytes <= kLeafStatBytes;
+        p.nrows = 0;
+        for (int n = 0; n < T; ++n)
+            if (p.leaves || ((p.internal[n >> 5] >> (n & 31)) & 1u)) p.rows[p.nrows++] = (uint8_t)n;
     }
     hipStream_t sm = (hipStream_t)stream;
     if (T > 1) {
-        const dim3 grid((unsigned)p.nchunk, (unsigned)T, (unsigned)B);
+        const dim3 grid((unsigned)p.nchunk, (unsigned)p.nrows, (unsigned)B);
         if (dtype == MEDUSA_BF16)
             hipLaunchKernelGGL(accept_stats_kernel<bf16_t>, grid, dim3(kThreads), 0, sm, p);
         else
