@@ -293,6 +293,12 @@ def main():
         "stages": stages,
     }
 
+    peaks = measure_peaks(mv, dev)
+    result["measured_peaks"] = peaks
+    result["roofline"]["frac_of_measured"] = round(achieved / peaks["hbm_read_GBps"], 4)
+    rt = result["roofline_tree_attention"]
+    rt["frac_of_measured"] = round(rt["achieved"] / (peaks["mfma_bf16_TFLOPs"] if rt["bound"] == "mfma"
+                                                     else peaks["hbm_read_GBps"]), 4)
     result["next_rows"] = {
         "kv_commit": measure_commit(mv, wl, tree, kc, vc, kt, vt, plen, acc["best_node"],
                                     args.steps),
@@ -317,6 +323,37 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, hx, ax, tree, cand, vlog_np, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
     print(json.dumps(result), flush=True)
+
+
+def measure_peaks(mv, dev, read_mib=2048, reps=10):
+    """The two ceilings measured on this device with the library's probes: a
+    linear 16-byte-load read of read_mib MiB (more than the last-level
+    cache) and independent bf16 32x32x16 MFMA chains on every CU."""
+    import torch
+    sink = torch.empty(mv.lib.medusa_probe_sink_bytes() // 4, dtype=torch.int32, device=dev)
+    buf = torch.ones(read_mib << 18, dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        mv.probe_read(buf, sink)
+    ev[0].record()
+    for _ in range(reps):
+        mv.probe_read(buf, sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    read_gbs = buf.numel() * 4 * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del buf
+    iters = 16384
+    mv.probe_mfma(iters, sink)
+    ev[0].record()
+    flops = 0.0
+    for _ in range(reps):
+        flops += mv.probe_mfma(iters, sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    tflops = flops / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    return {"hbm_read_GBps": round(read_gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
+            "method": f"medusa_probe_read over {read_mib} MiB x {reps}; medusa_probe_mfma "
+                      f"{iters} iterations x {reps} (events on the launch stream)"}
 
 
 def time_call(fn, steps, nbytes):

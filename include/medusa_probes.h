@@ -1,0 +1,46 @@
+/*
+ * medusa_probes.h -- device peak probes for the verify step's roofline.
+ *
+ * The verify step's kernels are judged against two ceilings: HBM read
+ * bandwidth (the Medusa heads' weight stream, the KV prefix and the
+ * verification logits are read once each) and dense bf16 matrix-core
+ * throughput (the tree attention over long prefixes).  The published
+ * MI355X figures are 8 TB/s and 2.5 PFLOP/s; these calls measure what the
+ * device delivers to kernels of the same access pattern, so that a kernel's
+ * fraction can be stated against both.  They compute nothing of the method.
+ * Same conventions as medusa_verify.h (device pointers, caller-owned memory,
+ * asynchronous on `stream`, status codes).
+ */
+#ifndef MEDUSA_PROBES_H
+#define MEDUSA_PROBES_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bytes of the device scratch `sink` that the probes write (one value per
+ * thread, so that no load or product can be optimised away). */
+size_t medusa_probe_sink_bytes(void);
+
+/* One linear pass of 16-byte loads over buf (device, 16-byte aligned,
+ * bytes > 0 a multiple of 16): every byte read once; one workgroup of 1024
+ * threads per CU streams its contiguous share with 4 loads in flight per
+ * thread.  Time it with events; bytes / time is the streaming read
+ * bandwidth. */
+int medusa_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
+
+/* 256 workgroups of four waves (one per SIMD), each wave running eight
+ * independent chains of `iters` v_mfma_f32_32x32x16_bf16 on register
+ * operands (no memory traffic); medusa_probe_mfma_flops(iters) is the work
+ * of one call.
+ * MEDUSA_ERR_PARAM when iters < 1. */
+int medusa_probe_mfma(int iters, void *sink, void *stream);
+double medusa_probe_mfma_flops(int iters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_PROBES_H */

@@ -32,6 +32,8 @@ EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
            "tree_accept", "tree_accept_workspace_bytes", "tree_commit_kv", "medusa_sample_token",
            "medusa_verify_forward", "medusa_verify_forward_workspace_bytes", "medusa_status_str",
            "medusa_abi_version"]
+PROBE_EXPORTS = ["medusa_probe_sink_bytes", "medusa_probe_read", "medusa_probe_mfma",
+                 "medusa_probe_mfma_flops"]
 
 
 class MedusaError(RuntimeError):
@@ -73,6 +75,14 @@ def _load() -> ctypes.CDLL:
     L.medusa_status_str.argtypes = [I]
     L.medusa_status_str.restype = ctypes.c_char_p
     L.medusa_abi_version.restype = I
+    L.medusa_probe_sink_bytes.argtypes = []
+    L.medusa_probe_sink_bytes.restype = Z
+    L.medusa_probe_read.argtypes = [P, Z, P, P]
+    L.medusa_probe_read.restype = I
+    L.medusa_probe_mfma.argtypes = [I, P, P]
+    L.medusa_probe_mfma.restype = I
+    L.medusa_probe_mfma_flops.argtypes = [I]
+    L.medusa_probe_mfma_flops.restype = ctypes.c_double
     for f in ("medusa_heads_topk", "medusa_heads_topk_noalloc", "medusa_heads_topk_root",
               "medusa_heads_stage1",
               "medusa_heads_stage2", "medusa_heads_stage2_stream", "medusa_heads_stage2_merge",
@@ -358,3 +368,20 @@ def medusa_verify_forward(h0: torch.Tensor, layers: Sequence[Dict[str, torch.Ten
         _ptr(out.get("k_tree")), _ptr(out.get("v_tree")), _ptr(ws), ws.numel(), _stream(stream))
     _check("medusa_verify_forward", rc)
     return out
+
+
+# ---------------------------------------------------------------------------
+# peak probes (include/medusa_probes.h)
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One linear 16-byte-load pass over buf (device)."""
+    _need(buf, "buf")
+    rc = lib.medusa_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                               _stream(stream))
+    _check("medusa_probe_read", rc)
+
+
+def probe_mfma(iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Independent bf16 32x32x16 MFMA chains; returns the FLOPs of the call."""
+    rc = lib.medusa_probe_mfma(int(iters), _ptr(sink), _stream(stream))
+    _check("medusa_probe_mfma", rc)
+    return float(lib.medusa_probe_mfma_flops(int(iters)))

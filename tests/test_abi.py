@@ -11,8 +11,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "medusa_verify.h")
 
 
-def _declared():
-    txt = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "medusa_probes.h")
+
+
+def _declared(header=HEADER):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) - {"if", "sizeof"})
 
@@ -29,6 +32,21 @@ def test_every_declared_symbol_is_exported(mv):
     for n in names:
         assert hasattr(mv.lib, n), n
     assert set(names) == set(mv.EXPORTS)
+    probes = _declared(PROBE_HEADER)
+    assert set(probes) == set(mv.PROBE_EXPORTS)
+    for n in probes:
+        assert hasattr(mv.lib, n), n
+
+
+def test_probe_validation(mv):
+    L = mv.lib
+    assert L.medusa_probe_sink_bytes() >= 256 * 1024 * 4
+    assert L.medusa_probe_read(None, 16, FAKE, None) == -1
+    assert L.medusa_probe_read(FAKE, 15, FAKE, None) == -2
+    assert L.medusa_probe_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == -2
+    assert L.medusa_probe_mfma(0, FAKE, None) == -6
+    assert L.medusa_probe_mfma(1, None, None) == -1
+    assert L.medusa_probe_mfma_flops(10) == 256 * 4 * 8 * 10 * 32 * 32 * 16 * 2
 
 
 def test_status_strings_and_version(mv):
