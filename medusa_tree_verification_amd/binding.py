@@ -42,11 +42,11 @@ class MedusaError(RuntimeError):
         self.code = code
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run medusa_tree_verification_amd/build.py "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run medusa_tree_verification_amd/build.py "
                           "(or __graft_entry__.build())")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.medusa_heads_topk.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]
     L.medusa_heads_topk_root.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, Z, P]

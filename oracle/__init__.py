@@ -35,11 +35,16 @@ def build(force: bool = True) -> str:
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library; MEDUSA_ORACLE_LIB names another build of the same
+    source (the sanitizer build of the CPU tests)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("MEDUSA_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         D = ctypes.c_double

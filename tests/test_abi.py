@@ -22,8 +22,17 @@ def _declared(header=HEADER):
 
 @pytest.fixture(scope="module")
 def mv():
+    """The binding; MEDUSA_VERIFY_TEST_LIB names another build of the same
+    sources to check instead (the sanitizer build of test_sanitizers.py)."""
     from medusa_tree_verification_amd import binding
-    return binding
+    path = os.environ.get("MEDUSA_VERIFY_TEST_LIB")
+    if path:
+        saved = binding.lib
+        binding.lib = binding._load(path)
+        yield binding
+        binding.lib = saved
+    else:
+        yield binding
 
 
 def test_every_declared_symbol_is_exported(mv):
