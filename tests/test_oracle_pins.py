@@ -518,6 +518,11 @@ def test_sample_special_cases():
     for uu in us:
         o = oracle.sample_token(np.zeros((1, 1, V), np.float32), [0], [uu], 0.7, "f32")
         assert o["token"][0] == int(np.floor(uu * V + 1e-9))
+    # u on a boundary: four equal logits give P(<= t) = (t + 1) / 4 exactly,
+    # and the draw is the first t whose P(<= t) exceeds u, so u = k / 4 -> k
+    for k in range(4):
+        o = oracle.sample_token(np.zeros((1, 1, 4), np.float32), [0], [k / 4], 1.0, "f32")
+        assert o["token"][0] == k
     # invalid row or u -> -1
     o = oracle.sample_token(x, [2, 0, -1], [0.5, 1.0, 0.5], 1.0, "f32")
     assert o["token"].tolist() == [-1, -1, -1]
