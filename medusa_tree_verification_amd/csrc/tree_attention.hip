@@ -164,8 +164,8 @@ struct RowState {
     float m;      // reference max (log2 units) the block scores are taken
                   // against; -inf before the first key; shared by the lane pair
     float l;      // this lane's part of the softmax denominator
-    f32x16 negr;  // -m in every element (0 while m = -inf): the accumulator
-                  // each block's first q.k product starts from
+    f32x16 negr;  // bf16: -m in every element (0 while m = -inf), the
+                  // accumulator each block's first q.k product starts from
 };
 
 // max over lanes l and l ^ 32 (v_permlane32_swap trades the upper half of
@@ -245,7 +245,18 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 #pragma unroll 1
     for (int sub = sub_lo; sub < sub_hi; ++sub) {   // 32-key halves of the stage
         const char *krow = Ks + (sub * 32 + col) * C::KS_STRIDE + h * 16;
-        f32x16 s = mma32_first(st.negr, *reinterpret_cast<const u32x4 *>(krow), qf[0], T{});
+        f32x16 s;
+        if constexpr (sizeof(T) == 2) {
+            s = mma32_first(st.negr, *reinterpret_cast<const u32x4 *>(krow), qf[0], T{});
+        } else {
+            // fp32 keeps no -m tile (its q.k takes more registers): the
+            // accumulator starts from -m broadcast on the spot
+            const float nr = st.m == -INFINITY ? 0.f : -st.m;
+            f32x16 init;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) init[r] = nr;
+            s = mma32_first(init, *reinterpret_cast<const u32x4 *>(krow), qf[0], T{});
+        }
 #pragma unroll
         for (int ks = 1; ks < C::NKS; ++ks) {
             const u32x4 a = *reinterpret_cast<const u32x4 *>(krow + ks * 32);
@@ -285,9 +296,11 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] -= sh;
             if (need) st.m = (st.m == -INFINITY ? 0.f : st.m) + sh;
-            const float nr = st.m == -INFINITY ? 0.f : -st.m;
+            if constexpr (sizeof(T) == 2) {
+                const float nr = st.m == -INFINITY ? 0.f : -st.m;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st.negr[r] = nr;
+                for (int r = 0; r < 16; ++r) st.negr[r] = nr;
+            }
         }
         if constexpr (sizeof(T) == 2) {
             // the probabilities packed to bf16 for the P V product; the row
