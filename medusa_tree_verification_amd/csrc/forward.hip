@@ -374,7 +374,10 @@ constexpr int kBigSK = 64;          // k per stage (two k-steps of 32)
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) const void *gbl_ptr_t;
 
-// s_waitcnt immediates: vmcnt(0) and vmcnt(16), lgkmcnt and expcnt untouched
+// s_waitcnt immediates: vmcnt(0) and vmcnt(16), lgkmcnt and expcnt untouched.
+// They count every vector-memory operation of the wave, so gemm_big_kernel
+// may issue none but its stage loads before its last barrier
+// (tests/test_kernel_resources.py checks the compiled kernel for that).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
 // workgroup barrier without memory fences; the compiler may move no memory

@@ -52,13 +52,23 @@ def _device_asm(src, tmp):
     return open(out).read()
 
 
-def test_no_kernel_spills_to_scratch(tmp_path):
+@pytest.fixture(scope="module")
+def asms(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not found")
+    tmp = str(tmp_path_factory.mktemp("asm"))
     with ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
-        asms = list(ex.map(lambda s: _device_asm(s, str(tmp_path)), SOURCES))
+        return dict(zip(SOURCES, ex.map(lambda s: _device_asm(s, tmp), SOURCES)))
+
+
+def _function(asm: str, name: str) -> str:
+    start = asm.index("\n" + name + ":")
+    return asm[start:asm.index(".Lfunc_end", start)]
+
+
+def test_no_kernel_spills_to_scratch(asms):
     seen = 0
-    for src, asm in zip(SOURCES, asms):
+    for src, asm in asms.items():
         for k in _kernels(asm):
             seen += 1
             assert k.get(".vgpr_spill_count", "0") == "0", (src, k)
@@ -107,3 +117,17 @@ def test_attention_staging_schedule(PD, nstage):
 def test_shipped_prefetch_depth_is_two():
     src = open(os.path.join(CSRC, "tree_attention.hip")).read()
     assert re.search(r"constexpr int kPD = 2;", src)
+
+
+def test_big_gemm_waits_only_on_its_stage_loads(asms):
+    """gemm_big_kernel waits on the vector-memory counter with fixed
+    immediates (all of this wave's loads, or all but the 16 of one stage)
+    and crosses its barriers without fences; that is right only while the
+    stage loads are the wave's only vector-memory operations in flight.  So
+    up to its last barrier the kernel may issue no other vector-memory
+    instruction than the direct-to-LDS stage loads."""
+    body = _function(asms["forward.hip"], "_ZN6medusa12_GLOBAL__N_115gemm_big_kernelENS0_8GemmArgsE")
+    last_barrier = body.rindex("s_barrier")
+    vmem = re.findall(r"^\s+((?:global|buffer|flat|scratch)_\w+)", body[:last_barrier], re.M)
+    assert vmem and set(vmem) == {"global_load_lds_dwordx4"}, sorted(set(vmem))
+    assert "s_waitcnt vmcnt(16)" in body and "s_waitcnt vmcnt(0)" in body
