@@ -489,9 +489,10 @@ def cpu_baseline(wl, hx, ax, tree, cand, vlog_np, budget_s):
             "stage_s": {"heads": round(t_heads, 3), "tree_attention": round(t_attn, 3),
                         "tree_accept": round(t_acc, 3)},
             "sample": f"one verify step of {wl.name}: heads (all {wl.B} sequences, "
-                      f"{wl.K} heads) and acceptance in full; tree attention on every "
-                      f"{stride}-th of its {nrows} output rows ({len(sample)} rows, "
-                      f"time scaled to all rows)"}
+                      f"{wl.K} heads) and acceptance in full; tree attention on "
+                      + (f"all {nrows} output rows" if stride == 1 else
+                         f"every {stride}th of its {nrows} output rows ({len(sample)} rows, "
+                         f"time scaled to all rows)")}
 
 
 if __name__ == "__main__":
