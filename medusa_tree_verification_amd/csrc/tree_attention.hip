@@ -25,6 +25,8 @@
 //   - P^T goes straight from the S^T accumulators into the B operand, V^T
 //     comes from LDS, where V is stored transposed (and, for bf16, with its
 //     4-key groups reordered so each lane reads one 16-byte chunk).
+#include <type_traits>
+
 #include "common.h"
 
 namespace medusa {
@@ -335,25 +337,37 @@ __device__ __forceinline__ void attend_stage(const char *lds, const u32x4 (&qf)[
     }
 }
 
-// NW waves are launched per workgroup; the first ks * p.W of them own query
-// rows (with ks = 2, two waves per row tile, one per 32-key half of each
-// stage), all of them share the staging of K/V.
-template <typename T, int DH, int NW>
-__global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams p) {
-    using C = Cfg<T, DH>;
-    constexpr int NT = NW * kWave;
-    __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
-    __shared__ __attribute__((aligned(16))) uint8_t par[MEDUSA_MAX_TREE];
+// What a workgroup and each of its lanes own.  Block ids are remapped so
+// that the m-tiles and splits of one (b, kv head) run on the same XCD; with
+// the key split (ks = 2) waves w and w + W share rows, wave group kgrp taking
+// the 32-key half kgrp of every stage.
+struct Tile {
+    int b, kvh, split, rwave, kgrp, row, t, hq;
+    bool rvalid, computes, last;
+    int kbeg, kend, nsb;
+    uint64_t mw0, mw1, mw2, mw3;   // the lane's ancestor-or-self bits over the tree keys
+};
 
+// Work set-up shared by both attention kernels: decodes the block id, loads
+// the lane's query row into qf (pre-scaled into the exponent's frame by
+// scale * log2 e; bf16: rounded to bf16 once), writes the parent table to
+// LDS, records out-of-range prefix lengths (block 0) and the tree mask
+// (block 0, when asked), and builds the lane's ancestor bitmask.  Returns
+// false when the block's prefix split is empty.  Every thread reaches the
+// one barrier inside.
+template <typename T, int DH>
+__device__ __forceinline__ bool tile_setup(const AttnParams &p, uint8_t *par,
+                                           u32x4 (&qf)[Cfg<T, DH>::NKS], Tile &tl) {
+    using C = Cfg<T, DH>;
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid % kWave, wave = tid / kWave;
 
     // logical block -> (b, kv head, split, m-tile), m-tile fastest
     const uint32_t lid = xcd_logical_id(blockIdx.x, (uint32_t)p.nwg);
     const int mt = (int)(lid % p.nmt);
-    const int split = (int)((lid / p.nmt) % p.nsplit);
-    const int kvh = (int)((lid / ((uint32_t)p.nmt * p.nsplit)) % p.Hkv);
-    const int b = (int)(lid / ((uint32_t)p.nmt * p.nsplit * p.Hkv));
+    tl.split = (int)((lid / p.nmt) % p.nsplit);
+    tl.kvh = (int)((lid / ((uint32_t)p.nmt * p.nsplit)) % p.Hkv);
+    tl.b = (int)(lid / ((uint32_t)p.nmt * p.nsplit * p.Hkv));
 
     // The prefix length, this lane's query row and the parent table are
     // loaded together, before the first wait.  The parent table
@@ -362,24 +376,24 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
     // for it then does not wait for them.
     static_assert(MEDUSA_MAX_TREE % 4 == 0 && MEDUSA_MAX_TREE / 4 <= 4 * kWave, "parent words");
     const uint32_t parw = tid < MEDUSA_MAX_TREE / 4 ? reinterpret_cast<const uint32_t *>(p.parent)[tid] : 0u;
-    const int Lraw = p.prefix_len[b];
+    const int Lraw = p.prefix_len[tl.b];
     const int col = lane & 31, h = lane >> 5;
-    // with the key split, waves w and w + W share rows: wave group kgrp takes
-    // the 32-key half kgrp of every stage
-    const int rwave = wave % p.W, kgrp = wave / p.W;
-    const int row = mt * 32 * p.W + rwave * 32 + col;
-    const bool rvalid = kgrp < p.ks && row < p.M;
-    const int g = rvalid ? row / p.T : 0;
-    const int t = rvalid ? row % p.T : 0;
-    const int hq = kvh * p.G + g;
-    u32x4 qf[C::NKS];
+    tl.rwave = wave % p.W;
+    tl.kgrp = wave / p.W;
+    tl.row = mt * 32 * p.W + tl.rwave * 32 + col;
+    tl.computes = tl.kgrp < p.ks;
+    tl.rvalid = tl.computes && tl.row < p.M;
+    const int g = tl.rvalid ? tl.row / p.T : 0;
+    tl.t = tl.rvalid ? tl.row % p.T : 0;
+    tl.hq = tl.kvh * p.G + g;
     {
         // one resource over the kv head's M query rows (a uniform base: a
         // per-lane resource would need a loop over the distinct lanes);
         // lanes without a row read past its end, which returns 0
-        const T *qkv = (const T *)p.q + ((size_t)b * p.Hq + (size_t)kvh * p.G) * p.T * DH;
+        const T *qkv = (const T *)p.q + ((size_t)tl.b * p.Hq + (size_t)tl.kvh * p.G) * p.T * DH;
         const auto qr = make_rsrc(qkv, (uint32_t)((size_t)p.M * DH * sizeof(T)));
-        const uint32_t qoff = rvalid ? (uint32_t)(((size_t)row * DH + h * C::KC) * sizeof(T)) : 0xFFFFF000u;
+        const uint32_t qoff =
+            tl.rvalid ? (uint32_t)(((size_t)tl.row * DH + h * C::KC) * sizeof(T)) : 0xFFFFF000u;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks)
             qf[ks] = buf_ld16(qr, qoff + (uint32_t)(ks * C::KSTEP * sizeof(T)));
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
         *p.err = bad;
     }
     const int L = Lraw < 0 ? 0 : (Lraw > p.Lcap ? p.Lcap : Lraw);
-    const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
+    tl.nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;
     __syncthreads();
     if (p.mask_out && lid == 0) {
         const int W = (p.T + 63) / 64;
@@ -406,13 +420,13 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
             for (int k = 0; k < W; ++k) p.mask_out[(size_t)n * W + k] = w[k];
         }
     }
-    if (split >= nsb) return;
-    const int kbeg = split * p.chunk;
-    const int kend = kbeg + p.chunk < L ? kbeg + p.chunk : L;
-    const bool last = split == nsb - 1;
+    if (tl.split >= tl.nsb) return false;
+    tl.kbeg = tl.split * p.chunk;
+    tl.kend = tl.kbeg + p.chunk < L ? tl.kbeg + p.chunk : L;
+    tl.last = tl.split == tl.nsb - 1;
 
     uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
-    for (int a = t, guard = 0; guard <= p.T; a = par[a], ++guard) {
+    for (int a = tl.t, guard = 0; guard <= p.T; a = par[a], ++guard) {
         const uint64_t bit = 1ull << (a & 63);
         const int wi = a >> 6;
         mw0 |= wi == 0 ? bit : 0ull;
@@ -421,23 +435,88 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
         mw3 |= wi == 3 ? bit : 0ull;
         if (par[a] == 255) break;   // a is the root
     }
+    tl.mw0 = mw0;
+    tl.mw1 = mw1;
+    tl.mw2 = mw2;
+    tl.mw3 = mw3;
 
-    // Q pre-scaled into the exponent's frame, scale * log2(e) (bf16: rounded
-    // to bf16 once)
-    {
-        const float cs = p.c;
+    const float cs = p.c;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks)
+    for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t v = qf[ks][w];
-                if constexpr (sizeof(T) == 2)
-                    qf[ks][w] = pack_bf16x2(__uint_as_float(v << 16) * cs,
-                                            __uint_as_float(v & 0xFFFF0000u) * cs);
-                else
-                    qf[ks][w] = __float_as_uint(__uint_as_float(v) * cs);
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t v = qf[ks][w];
+            if constexpr (sizeof(T) == 2)
+                qf[ks][w] = pack_bf16x2(__uint_as_float(v << 16) * cs,
+                                        __uint_as_float(v & 0xFFFF0000u) * cs);
+            else
+                qf[ks][w] = __float_as_uint(__uint_as_float(v) * cs);
+        }
+    return true;
+}
+
+// The tree ancestor bits of tree-key block wi (64 keys).
+__device__ __forceinline__ uint64_t tree_word(const Tile &tl, int wi) {
+    return wi == 0 ? tl.mw0 : wi == 1 ? tl.mw1 : wi == 2 ? tl.mw2 : tl.mw3;
+}
+
+// Writes this lane's finished O^T columns (nsb == 1: normalised output;
+// otherwise fp32 partials with the split's (max, sum)).
+template <typename T, int DH>
+__device__ __forceinline__ void store_rows(const AttnParams &p, const Tile &tl,
+                                           const f32x16 (&o)[Cfg<T, DH>::NDT], float m, float ltot,
+                                           int h) {
+    using C = Cfg<T, DH>;
+    const size_t orow = ((size_t)tl.b * p.Hq + tl.hq) * p.T + tl.t;
+    if (tl.nsb == 1) {
+        const float inv = 1.0f / ltot;
+        T *dst = (T *)p.out + orow * DH;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                T *d4 = dst + dt * 32 + 8 * i + 4 * h;
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+                    const uint32_t hi = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(d4) = u32x2{lo, hi};
+                } else {
+                    *reinterpret_cast<f32x4 *>(d4) =
+                        f32x4{o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
+                              o[dt][4 * i + 3] * inv};
+                }
             }
+    } else {
+        const size_t prow = (size_t)tl.split * p.B * p.Hq * p.T + orow;
+        float *dst = p.part_o + prow * DH;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4 *>(dst + dt * 32 + 8 * i + 4 * h) =
+                    f32x4{o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]};
+        if (h == 0) p.part_ml[prow] = make_float2(m, ltot);
     }
+}
+
+// NW waves are launched per workgroup; the first ks * p.W of them own query
+// rows (with ks = 2, two waves per row tile, one per 32-key half of each
+// stage), all of them share the staging of K/V.
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams p) {
+    using C = Cfg<T, DH>;
+    constexpr int NT = NW * kWave;
+    __shared__ __attribute__((aligned(16))) char lds[2][C::LDS_BYTES];   // double buffer
+    __shared__ __attribute__((aligned(16))) uint8_t par[MEDUSA_MAX_TREE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    u32x4 qf[C::NKS];
+    Tile tl;
+    if (!tile_setup<T, DH>(p, par, qf, tl)) return;
+    const int b = tl.b, kvh = tl.kvh, kgrp = tl.kgrp, rwave = tl.rwave;
+    const int kbeg = tl.kbeg, kend = tl.kend;
+    const bool last = tl.last;
     f32x16 o[C::NDT];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{};
@@ -452,7 +531,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
     const int ntree = p.T;        // the lambdas below take no reference to p:
                                   // that would copy the parameter block to scratch
     const int nstage = npre + (last ? (ntree + kBN - 1) / kBN : 0);
-    const bool computes = kgrp < p.ks;
+    const bool computes = tl.computes;
     const int sub_lo = p.ks == 2 ? kgrp : 0, sub_hi = p.ks == 2 ? kgrp + 1 : 2;
 
     // PD register sets of staged K/V: the loads of a stage are issued PD
@@ -510,7 +589,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
                 } else {
                     const int wi = sidx - npre;
                     kind = 1;
-                    mword = wi == 0 ? mw0 : wi == 1 ? mw1 : wi == 2 ? mw2 : mw3;
+                    mword = tree_word(tl, wi);
                 }
                 const bool masked = kind == 1 || klim < kBN;
                 attend_stage<T, DH>(lds[sidx & 1], qf, o, st, lane, masked, kind, klim, mword,
@@ -551,37 +630,328 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
         ltot = ltot * a0 + ml1.y * a1;
         st.m = mnew;
     }
-    if (!rvalid || !computes) return;
-    const size_t orow = ((size_t)b * p.Hq + hq) * p.T + t;
-    if (nsb == 1) {
-        const float inv = 1.0f / ltot;
-        T *dst = (T *)p.out + orow * DH;
+    if (!tl.rvalid || !computes) return;
+    store_rows<T, DH>(p, tl, o, st.m, ltot, lane >> 5);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel: bf16, dh = 128, m-tiles of at least five row waves (one
+// wave per 32 query rows, each taking both 32-key halves of every stage).
+//
+// K/V stages go from global memory straight into LDS (16-byte direct loads,
+// no staging registers), four stage buffers deep; the loads of stage s + 3
+// are issued while stage s is computed.  K and V rows stay key-major.  The
+// V^T fragments of the P V product are read with the LDS transpose read
+// (ds_read_b64_tr_b16): within each 16 lanes, lane 4r + q addresses four
+// consecutive 16-bit elements of row r, and lane i receives element i of the
+// four rows, so one read gives a lane four consecutive keys of one dh
+// column.  The 16-byte chunks of a row are XOR-swizzled (K: chunk c of key
+// row r at slot c ^ (r mod 16); V: at slot c ^ 4 (r mod 4)) so that the
+// K fragment reads (16 key rows per 16 lanes, one chunk each) and the
+// transpose reads (4 key rows x 64 bytes per 32 lanes) hit distinct banks.
+//
+// Per wave the 32-key blocks form a pipeline: block j + 1's scores are
+// computed on the matrix cores while block j's row max is found, and the
+// P V product of block j's first 16 keys runs while the second 16 are
+// exponentiated.  Blocks past a stage boundary come from the next stage's
+// buffer, which the previous barrier made visible; one barrier per stage.
+constexpr int kPipeNB = 4;                                     // LDS stage buffers
+constexpr int kPipeRB = 128 * 2;                               // bytes per K or V row
+constexpr int kPipeOp = kBN * kPipeRB;                         // one operand of one stage
+constexpr int kPipeLoads = 2 * (kPipeOp / 1024) / kMaxWaves;   // loads per wave and stage
+static_assert(kPipeLoads == 4, "the stage wait below counts four loads per wave");
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// s_waitcnt: at most one stage of this wave's loads (kPipeLoads) still in
+// flight, every LDS read returned.  The stage loads are the only vector
+// memory operations inside the stage loop.
+__device__ __forceinline__ void pipe_wait_stage() { __builtin_amdgcn_s_waitcnt(0x0074); }
+__device__ __forceinline__ void pipe_wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// workgroup barrier without memory fences; no memory access moves across it
+__device__ __forceinline__ void pipe_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ u32x4 pipe_ld16(const char *lds, uint32_t off) {
+    return *reinterpret_cast<const u32x4 *>(lds + off);
+}
+__device__ __forceinline__ u32x2 pipe_ld_tr(const char *lds, uint32_t off) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t *)((__attribute__((address_space(3))) char *)lds + off));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// The per-lane LDS byte addresses of the fragments (the buffer, half and
+// k-step parts are immediate offsets).
+struct PipeLane {
+    uint32_t ka[8];   // K fragment of k-step ks: key row col, chunk 2 ks + h
+    uint32_t va[4];   // V^T transpose read of dh tile dt
+};
+
+// One 32-key block.  sc holds its scores against the current reference; the
+// next block's scores go to sn (K rows at koff in buffer kbuf); this block's
+// V rows are at voff in buffer vbuf.
+__device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, uint32_t koff,
+                                           uint32_t voff, f32x16 &sc, f32x16 &sn,
+                                           const u32x4 (&qf)[8],
+                                           f32x16 (&o)[4], RowState &st, const PipeLane &pl,
+                                           bool masked, uint32_t bits) {
+    if (masked) {   // the same in every lane
+        // s[r] is key 4h + 8 (r / 4) + r % 4 of the block; bit k of bits
+        // tells whether key 4h + k is visible to this lane's query
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                T *d4 = dst + dt * 32 + 8 * i + 4 * h;
-                if constexpr (sizeof(T) == 2) {
-                    const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
-                    const uint32_t hi = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(d4) = u32x2{lo, hi};
-                } else {
-                    *reinterpret_cast<f32x4 *>(d4) =
-                        f32x4{o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
-                              o[dt][4 * i + 3] * inv};
-                }
-            }
-    } else {
-        const size_t prow = (size_t)split * p.B * p.Hq * p.T + orow;
-        float *dst = p.part_o + prow * DH;
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<f32x4 *>(dst + dt * 32 + 8 * i + 4 * h) =
-                    f32x4{o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]};
-        if (h == 0) p.part_ml[prow] = make_float2(st.m, ltot);
+        for (int r = 0; r < 16; ++r)
+            sc[r] = (bits >> (8 * (r >> 2) + (r & 3))) & 1u ? sc[r] : -INFINITY;
     }
+    // the next block's scores start from -m (the reference as it is now)
+    sn = mma32_first(st.negr, pipe_ld16(kbuf, pl.ka[0] + koff), qf[0], bf16_t{});
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) mma32_step(sn, pipe_ld16(kbuf, pl.ka[ks] + koff), qf[ks], bf16_t{});
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = pair_max(mx);
+    // lazy reference (as in attend_stage); a move also applies to the next
+    // block's scores, which were taken against the old one
+    const bool need = st.m == -INFINITY ? mx > -INFINITY : mx > 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+        const float sh = need ? mx : 0.f;
+        const float alpha = !need ? 1.f : (st.m == -INFINITY ? 0.f : fast_exp2(-sh));
+        st.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sc[r] -= sh;
+            sn[r] -= sh;
+        }
+        if (need) st.m = (st.m == -INFINITY ? 0.f : st.m) + sh;
+        const float nr = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.negr[r] = nr;
+    }
+    // probabilities packed to bf16 for the P V product (k-step mm: keys
+    // 16 mm + 4h + 8 (e / 4) + e % 4 in element e of the B operand); the row
+    // sum takes the same bf16 values
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc = st.l;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        u32x4 pk;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t v = pack_bf16x2(fast_exp2(sc[8 * mm + 2 * w]), fast_exp2(sc[8 * mm + 2 * w + 1]));
+            pk[w] = v;
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), ones, acc, false);
+        }
+        // A operand: V^T rows 32 dt + col; elements 0-3 keys 16 mm + 4h + 0..3,
+        // elements 4-7 keys 16 mm + 4h + 8..11 (two transpose reads)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const u32x2 a0 = pipe_ld_tr(vbuf, pl.va[dt] + voff + (uint32_t)(16 * mm) * kPipeRB);
+            const u32x2 a1 = pipe_ld_tr(vbuf, pl.va[dt] + voff + (uint32_t)(16 * mm + 8) * kPipeRB);
+            mma32_step(o[dt], u32x4{a0[0], a0[1], a1[0], a1[1]}, pk, bf16_t{});
+        }
+    }
+    st.l = acc;
+}
+
+// The four stage buffers, K and V (16 KiB each), as separate LDS variables
+// named by compile-time index only: the compiler then tells a read of one
+// buffer from a direct load into another, and adds no wait for loads still
+// landing elsewhere.  (Only the pipelined kernel uses them.)
+__shared__ __attribute__((aligned(1024))) char pipe_k0[kPipeOp], pipe_k1[kPipeOp], pipe_k2[kPipeOp],
+    pipe_k3[kPipeOp];
+__shared__ __attribute__((aligned(1024))) char pipe_v0[kPipeOp], pipe_v1[kPipeOp], pipe_v2[kPipeOp],
+    pipe_v3[kPipeOp];
+template <int B>
+__device__ __forceinline__ char *pipe_kbuf() {
+    if constexpr (B == 0) return pipe_k0;
+    else if constexpr (B == 1) return pipe_k1;
+    else if constexpr (B == 2) return pipe_k2;
+    else return pipe_k3;
+}
+template <int B>
+__device__ __forceinline__ char *pipe_vbuf() {
+    if constexpr (B == 0) return pipe_v0;
+    else if constexpr (B == 1) return pipe_v1;
+    else if constexpr (B == 2) return pipe_v2;
+    else return pipe_v3;
+}
+
+// Both blocks of one stage held in buffer B (the second block's successor
+// is the first block of the next stage, in buffer B + 1).  The scores
+// alternate between sc and sn, so after a stage the current ones are in sc
+// again.  masked (the same in every lane): apply vis, whose bit k is set
+// when key k of the stage is visible to this lane's query.
+template <int B>
+__device__ __forceinline__ void pipe_stage(f32x16 &sc, f32x16 &sn,
+                                           const u32x4 (&qf)[8], f32x16 (&o)[4], RowState &st,
+                                           const PipeLane &pl, int h, bool masked, uint64_t vis) {
+    const char *kc = pipe_kbuf<B>(), *vc = pipe_vbuf<B>();
+    const char *kn = pipe_kbuf<(B + 1) & (kPipeNB - 1)>();
+    // The V buffers lie past the reach of the 16-bit read offset, so each
+    // stage forms its own four V addresses; the empty asm hides the lane
+    // offsets' origin, which keeps the compiler from holding all sixteen
+    // (buffer, dh tile) addresses in registers across the loop.
+    PipeLane ps = pl;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) asm volatile("" : "+v"(ps.va[dt]));
+    pipe_block(kc, vc, kPipeOp / 2, 0, sc, sn, qf, o, st, ps, masked, (uint32_t)(vis >> (4 * h)));
+    pipe_block(kn, vc, 0, kPipeOp / 2, sn, sc, qf, o, st, ps, masked, (uint32_t)(vis >> (32 + 4 * h)));
+}
+
+// Where a workgroup's stages come from, and this wave's share of their loads.
+struct PipeSrc {
+    const char *kcb, *vcb, *ktb, *vtb;   // prefix K/V and tree K/V rows of (b, kv head)
+    int kbeg, kend, npre, nstage, ntree;
+    int wave;
+    uint32_t ok0, ok1, ov0, ov1;         // byte offsets of this lane's loads within a stage
+};
+
+// Stage sidx into buffer B.  The wave issues instructions j = wave and
+// wave + 8 of each operand, each moving key rows 4 j .. 4 j + 3 (lane l: row
+// 4 j + l / 16, LDS slot l % 16, which holds chunk slot ^ swizzle(row)).  The
+// loads go through a buffer resource covering the stage's keys only, so
+// rows past them read as zeros (their scores are masked; zero V rows add
+// nothing), and the lane offsets stay the same for every stage.  Stages past
+// the last load the last one again, into a buffer nothing reads, so that
+// every stage issues the same loads.
+template <int B>
+__device__ __forceinline__ void pipe_issue(const PipeSrc &ps, int sidx) {
+    char *dk = pipe_kbuf<B>(), *dv = pipe_vbuf<B>();
+    const int se = sidx < ps.nstage ? sidx : ps.nstage - 1;
+    const char *kb, *vb;
+    int nv;
+    if (se < ps.npre) {
+        const int k0 = ps.kbeg + se * kBN;
+        nv = ps.kend - k0 < kBN ? ps.kend - k0 : kBN;
+        kb = ps.kcb + (size_t)k0 * kPipeRB;
+        vb = ps.vcb + (size_t)k0 * kPipeRB;
+    } else {
+        const int tb = (se - ps.npre) * kBN;
+        nv = ps.ntree - tb < kBN ? ps.ntree - tb : kBN;
+        kb = ps.ktb + (size_t)tb * kPipeRB;
+        vb = ps.vtb + (size_t)tb * kPipeRB;
+    }
+    const uint32_t nbytes = (uint32_t)nv * kPipeRB;
+    const auto kr = make_rsrc(kb, nbytes), vr = make_rsrc(vb, nbytes);
+    typedef __attribute__((address_space(3))) void *lds_vptr_t;
+    const uint32_t d0 = (uint32_t)ps.wave * 1024u, d1 = (uint32_t)(ps.wave + 8) * 1024u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_vptr_t)(dk + d0), 16, ps.ok0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_vptr_t)(dv + d0), 16, ps.ov0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_vptr_t)(dk + d1), 16, ps.ok1, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_vptr_t)(dv + d1), 16, ps.ov1, 0, 0, 0);
+}
+
+// One pipeline step: stage sidx from buffer B.  Loads of stage sidx + 3 go
+// out, both blocks are computed (the prefix tail and the tree stages with
+// vis applied), the wave waits for its loads of stage sidx + 2, barrier.
+template <int B>
+__device__ __forceinline__ void pipe_step(const PipeSrc &ps, int sidx, bool computes, int nfull,
+                                          uint64_t tw0, uint64_t tw1, uint64_t tw2, uint64_t tw3,
+                                          f32x16 &sc, f32x16 &sn, const u32x4 (&qf)[8],
+                                          f32x16 (&o)[4], RowState &st, const PipeLane &pl, int h) {
+    pipe_issue<(B + 3) & (kPipeNB - 1)>(ps, sidx + 3);
+    if (computes) {
+        // the prefix tail: its first klim (< 64) keys; a tree stage: the
+        // lane's ancestor-or-self bits
+        const bool masked = sidx >= nfull;
+        const int klim = ps.kend - (ps.kbeg + sidx * kBN);
+        const int wi = sidx - ps.npre;
+        const uint64_t tw = wi <= 0 ? tw0 : wi == 1 ? tw1 : wi == 2 ? tw2 : tw3;
+        const uint64_t vis = !masked ? 0ull : sidx < ps.npre ? (1ull << klim) - 1ull : tw;
+        pipe_stage<B>(sc, sn, qf, o, st, pl, h, masked, vis);
+    }
+    pipe_wait_stage();
+    pipe_barrier();
+}
+
+__global__ __launch_bounds__(kMaxWaves *kWave, 1) void tree_attn_pipe_kernel(AttnParams p) {
+    using T = bf16_t;
+    constexpr int DH = 128;
+    __shared__ __attribute__((aligned(16))) uint8_t par[MEDUSA_MAX_TREE];
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    u32x4 qf[8];
+    Tile tl;
+    if (!tile_setup<T, DH>(p, par, qf, tl)) return;
+    const bool computes = tl.computes;
+    const int col = lane & 31, h = lane >> 5;
+
+    PipeSrc ps;
+    {
+        const size_t bh = (size_t)tl.b * p.Hkv + tl.kvh;
+        ps.kcb = (const char *)p.kc + bh * (size_t)p.Lcap * kPipeRB;
+        ps.vcb = (const char *)p.vc + bh * (size_t)p.Lcap * kPipeRB;
+        ps.ktb = (const char *)p.kt + bh * (size_t)p.T * kPipeRB;
+        ps.vtb = (const char *)p.vt + bh * (size_t)p.T * kPipeRB;
+        ps.kbeg = tl.kbeg;
+        ps.kend = tl.kend;
+        ps.ntree = p.T;
+        ps.npre = (tl.kend - tl.kbeg + kBN - 1) / kBN;
+        ps.nstage = ps.npre + (tl.last ? (p.T + kBN - 1) / kBN : 0);
+        ps.wave = wave;
+        const int row0 = 4 * wave + (lane >> 4), row1 = row0 + 32;
+        const uint32_t cv = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
+        ps.ok0 = (uint32_t)(row0 * kPipeRB + ((lane & 15) ^ (row0 & 15)) * 16);
+        ps.ok1 = (uint32_t)(row1 * kPipeRB + ((lane & 15) ^ (row1 & 15)) * 16);
+        ps.ov0 = (uint32_t)row0 * kPipeRB + cv;
+        ps.ov1 = (uint32_t)row1 * kPipeRB + cv;
+    }
+    const int nfull = (tl.kend - tl.kbeg) / kBN;   // prefix stages with all 64 keys (no mask)
+    const int nstage = ps.nstage;
+    const uint64_t tw0 = tl.mw0, tw1 = tl.mw1, tw2 = tl.mw2, tw3 = tl.mw3;
+
+    PipeLane pl;
+    {
+        const uint32_t ky = (uint32_t)(h ^ (col & 15));
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) pl.ka[ks] = (uint32_t)col * kPipeRB + ((32u * ks) ^ (16u * ky));
+        const int r4 = (lane >> 2) & 3, q = lane & 3, gm = (lane >> 4) & 1;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            pl.va[dt] = (uint32_t)((4 * h + r4) * kPipeRB + (2 * gm + (q >> 1)) * 16 + (q & 1) * 8 +
+                                   64 * (dt ^ r4));
+    }
+
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    RowState st{-INFINITY, 0.f, f32x16{}};
+    f32x16 sc = f32x16{}, sn = f32x16{};
+
+    // block 0 (first 32 keys of stage 0) before the pipeline starts
+    pipe_issue<0>(ps, 0);
+    pipe_issue<1>(ps, 1);
+    pipe_issue<2>(ps, 2);
+    pipe_wait_stage();   // stages 0 and 1: this wave's loads
+    pipe_barrier();      // ... and every wave's
+    if (computes) {
+        sc = mma32_first(st.negr, pipe_ld16(pipe_k0, pl.ka[0]), qf[0], bf16_t{});
+#pragma unroll
+        for (int ks = 1; ks < 8; ++ks) mma32_step(sc, pipe_ld16(pipe_k0, pl.ka[ks]), qf[ks], bf16_t{});
+    }
+    // stage s in buffer s mod 4, named statically: the loop is unrolled by four
+    for (int s = 0; s < nstage; s += kPipeNB) {
+        pipe_step<0>(ps, s, computes, nfull, tw0, tw1, tw2, tw3, sc, sn, qf, o, st, pl, h);
+        if (s + 1 >= nstage) break;
+        pipe_step<1>(ps, s + 1, computes, nfull, tw0, tw1, tw2, tw3, sc, sn, qf, o, st, pl, h);
+        if (s + 2 >= nstage) break;
+        pipe_step<2>(ps, s + 2, computes, nfull, tw0, tw1, tw2, tw3, sc, sn, qf, o, st, pl, h);
+        if (s + 3 >= nstage) break;
+        pipe_step<3>(ps, s + 3, computes, nfull, tw0, tw1, tw2, tw3, sc, sn, qf, o, st, pl, h);
+    }
+    pipe_wait_all();   // the loads past the last stage are still writing LDS
+
+    const float ltot = st.l + __shfl_xor(st.l, 32);
+    if (!tl.rvalid) return;
+    store_rows<T, DH>(p, tl, o, st.m, ltot, h);
 }
 
 // Merge split partials of the rows whose prefix used more than one split:
@@ -756,8 +1126,12 @@ int launch_attn(const AttnParams &p, hipStream_t st) {
     // Eight waves (two per SIMD at <= 256 registers each): with few row
     // waves (ks * W <= 4) the others only stage K/V, which measured faster
     // than four waves at one per SIMD.
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, kMaxWaves>), dim3(p.nwg), dim3(kMaxWaves * kWave),
-                       0, st, p);
+    // bf16 with dh = 128 and every wave owning rows: the pipelined kernel
+    if (sizeof(T) == 2 && DH == 128 && p.ks == 1)
+        hipLaunchKernelGGL(tree_attn_pipe_kernel, dim3(p.nwg), dim3(kMaxWaves * kWave), 0, st, p);
+    else
+        hipLaunchKernelGGL((tree_attn_fwd_kernel<T, DH, kMaxWaves>), dim3(p.nwg),
+                           dim3(kMaxWaves * kWave), 0, st, p);
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (p.nsplit > 1) {
         const size_t rows = (size_t)p.B * p.Hq * p.T;

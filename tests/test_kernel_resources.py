@@ -19,6 +19,7 @@ import re
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -131,3 +132,127 @@ def test_big_gemm_waits_only_on_its_stage_loads(asms):
     vmem = re.findall(r"^\s+((?:global|buffer|flat|scratch)_\w+)", body[:last_barrier], re.M)
     assert vmem and set(vmem) == {"global_load_lds_dwordx4"}, sorted(set(vmem))
     assert "s_waitcnt vmcnt(16)" in body and "s_waitcnt vmcnt(0)" in body
+
+
+# ---------------------------------------------------------------------------
+# The pipelined bf16 dh = 128 kernel: LDS layout of a stage and its schedule.
+
+PIPE_RB, PIPE_OP = 256, 16384   # bytes per key row, bytes per operand and stage
+
+
+def _pipe_stage_lds(Kst, Vst):
+    """The K and V buffers (as 16-bit words) after every wave's direct loads
+    of one 64-key stage: wave w, instruction i moves key rows 4 (w + 8 i) ..
+    + 3, lane l landing at byte l * 16 of its kilobyte with chunk
+    (l % 16) ^ swizzle(row) of row 4 (w + 8 i) + l / 16."""
+    kl = np.full(PIPE_OP // 2, -1, np.int64)
+    vl = np.full(PIPE_OP // 2, -1, np.int64)
+    kg, vg = Kst.reshape(-1), Vst.reshape(-1)
+    for wave in range(8):
+        for lane in range(64):
+            row0 = 4 * wave + (lane >> 4)
+            cv = ((lane & 15) ^ (4 * (lane >> 4))) * 16
+            for i, row in enumerate((row0, row0 + 32)):
+                ok = row * PIPE_RB + ((lane & 15) ^ (row & 15)) * 16
+                ov = row * PIPE_RB + cv
+                dst = ((wave + 8 * i) * 1024 + lane * 16) // 2
+                assert (kl[dst:dst + 8] == -1).all() and (vl[dst:dst + 8] == -1).all()
+                kl[dst:dst + 8] = kg[ok // 2:ok // 2 + 8]
+                vl[dst:dst + 8] = vg[ov // 2:ov // 2 + 8]
+    return kl, vl
+
+
+def test_pipelined_attention_lds_fragments():
+    """Every lane's K fragment (ds_read_b128) and V^T fragment (two
+    ds_read_b64_tr_b16: within 16 lanes, lane i receives element i of the
+    four 8-byte rows addressed by lanes 4r + q) are the MFMA operands the
+    kernel assumes; every read stays inside its 16 KiB buffer and hits
+    distinct LDS banks per pass."""
+    rng = np.random.default_rng(3)
+    Kst = rng.integers(0, 1 << 16, size=(64, 128))
+    Vst = rng.integers(0, 1 << 16, size=(64, 128))
+    kl, vl = _pipe_stage_lds(Kst, Vst)
+    assert (kl >= 0).all() and (vl >= 0).all()
+    for sub in range(2):
+        for ks in range(8):
+            offs = []
+            for lane in range(64):
+                col, h = lane & 31, lane >> 5
+                off = col * PIPE_RB + ((32 * ks) ^ (16 * (h ^ (col & 15)))) + sub * 8192
+                assert off + 16 <= PIPE_OP
+                got = kl[off // 2:off // 2 + 8]
+                assert (got == Kst[32 * sub + col, 16 * ks + 8 * h:16 * ks + 8 * h + 8]).all()
+                offs.append(off)
+            for p in range(4):   # 16 lanes per pass, 16 distinct 16-byte bank groups
+                assert len({(a // 16) % 16 for a in offs[16 * p:16 * p + 16]}) == 16
+        for mm in range(2):
+            for dt in range(4):
+                A = np.zeros((64, 8), np.int64)
+                for rd in range(2):
+                    addr = []
+                    for lane in range(64):
+                        h, r4, q, gm = lane >> 5, (lane >> 2) & 3, lane & 3, (lane >> 4) & 1
+                        va = (4 * h + r4) * PIPE_RB + (2 * gm + (q >> 1)) * 16 + (q & 1) * 8 + 64 * (dt ^ r4)
+                        a = va + sub * 8192 + (16 * mm + 8 * rd) * PIPE_RB
+                        assert a + 8 <= PIPE_OP
+                        addr.append(a)
+                    for g in range(4):
+                        for i in range(16):
+                            for r in range(4):
+                                A[16 * g + i, 4 * rd + r] = vl[addr[16 * g + 4 * r + i // 4] // 2 + i % 4]
+                    for p in range(2):   # 32 lanes of 8 bytes per pass: all 64 banks
+                        banks = set()
+                        for a in addr[32 * p:32 * p + 32]:
+                            banks |= {(a // 4) % 64, (a // 4 + 1) % 64}
+                        assert len(banks) == 64
+                for lane in range(64):
+                    h = lane >> 5
+                    for e in range(8):
+                        key = 32 * sub + 16 * mm + 4 * h + 8 * (e // 4) + e % 4
+                        assert A[lane, e] == Vst[key, 32 * dt + (lane & 31)]
+                        # the same key as element e of the P^T operand: score
+                        # r = 8 mm + e of the lane (key 8 (r / 4) + 4 h + r % 4)
+                        r = 8 * mm + e
+                        assert key == 32 * sub + 8 * (r // 4) + 4 * h + r % 4
+
+
+@pytest.mark.parametrize("nstage", [1, 2, 3, 4, 5, 8, 131])
+def test_pipelined_attention_schedule(nstage):
+    """Four stage buffers, loads three stages ahead, one barrier per stage.
+    Before the first step stages 0-2 are issued, the wave waits for all but
+    the latest stage and a barrier follows; then block 0 is read.  Step s
+    issues stage s + 3 into buffer (s + 3) mod 4, reads stage s (buffer
+    s mod 4) and the first half of stage s + 1 (buffer (s + 1) mod 4), waits
+    for all but the latest stage's loads, barrier.  Every read must find its
+    stage in the buffer and landed before the last barrier; a buffer is
+    loaded again only after the last read of its previous stage, in an
+    earlier barrier interval."""
+    held = {}          # buffer -> stage it holds (or is receiving)
+    issued = []        # stages in issue order
+    landed = set()     # stages whose loads are complete
+    visible = set()    # stages landed before the last barrier
+    last_read = {}     # stage -> step of its last read (-1: before the first step)
+
+    def issue(t, step):
+        b = t % 4
+        prev = held.get(b)
+        if prev is not None:
+            assert last_read.get(prev, -2) < step, (t, prev, step)
+        held[b] = t
+        issued.append(t)
+
+    def read(t, step):
+        assert held[t % 4] == t and t in visible, (t, step, held)
+        last_read[t] = step
+
+    for t in range(3):
+        issue(t, -1)
+    landed.update(issued[:-1])
+    visible = set(landed)
+    read(0, -1)
+    for s in range(nstage):
+        issue(s + 3, s)
+        read(s, s)
+        read(s + 1, s)    # past the last stage: a reload of the last one, its result unused
+        landed.update(issued[:-1])
+        visible = set(landed)
