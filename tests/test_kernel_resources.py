@@ -256,3 +256,15 @@ def test_pipelined_attention_schedule(nstage):
         read(s + 1, s)    # past the last stage: a reload of the last one, its result unused
         landed.update(issued[:-1])
         visible = set(landed)
+
+
+def test_no_bit_cast_of_vector_elements():
+    """__builtin_bit_cast of an ext_vector element (v[i]) compiles to a cast
+    of element 0 whatever i is (seen in the attention kernel's row sums);
+    the sources must cast scalars instead."""
+    bad = []
+    for src in SOURCES + ["common.h"]:
+        for n, line in enumerate(open(os.path.join(CSRC, src)), 1):
+            if re.search(r"__builtin_bit_cast\([^,]+,\s*[\w.]+\[[^\]]+\]\s*\)", line):
+                bad.append(f"{src}:{n}: {line.strip()}")
+    assert not bad, bad
