@@ -254,6 +254,13 @@ def main():
     attn_bound = stages["tree_attention"]["bound"]
     attn_tf = flops / (per["tree_attention"] * 1e-3) / 1e12
     attn_gbs = nbytes["tree_attention"] / (per["tree_attention"] * 1e-3) / 1e9
+    # the library's choice: the pipelined kernel for bf16, dh = 128 and at
+    # least five 32-row waves per m-tile (G * T query rows per kv head)
+    row_waves = min((wl.Hq // wl.Hkv * T + 31) // 32, 8)
+    attn_main = ("tree_attn_pipe_kernel" if wl.dtype == W.BF16 and wl.dh == 128 and row_waves > 4
+                 else "tree_attn_fwd_kernel")
+    attn_kernel = (attn_main + " (+ tree_attn_combine_kernel when the prefix is split): "
+                   "the tree_attention call")
     result = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 2),
@@ -280,13 +287,11 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "roofline_tree_attention": (
-            {"kernel": "tree_attn_fwd_kernel (+ tree_attn_combine_kernel when the prefix is "
-                       "split): the tree_attention call", "bound": "mfma",
+            {"kernel": attn_kernel, "bound": "mfma",
              "achieved": round(attn_tf, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
              "frac": round(attn_tf / PEAK_MFMA_TFLOPS, 4), "hbm_GBps": round(attn_gbs, 1),
              "flops": int(flops)} if attn_bound == "mfma" else
-            {"kernel": "tree_attn_fwd_kernel (+ tree_attn_combine_kernel when the prefix is "
-                       "split): the tree_attention call", "bound": "hbm",
+            {"kernel": attn_kernel, "bound": "hbm",
              "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "TFLOPs": round(attn_tf, 1),
              "bytes": int(nbytes["tree_attention"])}),

@@ -168,6 +168,8 @@ struct RowState {
     float l;      // this lane's part of the softmax denominator
     f32x16 negr;  // bf16: -m in every element (0 while m = -inf), the
                   // accumulator each block's first q.k product starts from
+    float thr;    // the block max (relative to m) that moves m: -inf while
+                  // m = -inf, then 8 (pipelined kernel)
 };
 
 // max over lanes l and l ^ 32 (v_permlane32_swap trades the upper half of
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
     f32x16 o[C::NDT];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{};
-    RowState st{-INFINITY, 0.f, f32x16{}};
+    RowState st{-INFINITY, 0.f, f32x16{}, -INFINITY};
 
     // stages: prefix keys [kbeg, kend) in blocks of kBN, then (last split) the tree keys
     const T *kcb = (const T *)p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.Lcap * DH;
@@ -715,9 +717,10 @@ __device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, u
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
     mx = pair_max(mx);
-    // lazy reference (as in attend_stage); a move also applies to the next
-    // block's scores, which were taken against the old one
-    const bool need = st.m == -INFINITY ? mx > -INFINITY : mx > 8.0f;
+    // lazy reference (as in attend_stage, with the threshold kept in st.thr);
+    // a move also applies to the next block's scores, which were taken
+    // against the old one
+    const bool need = mx > st.thr;
     if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
         const float sh = need ? mx : 0.f;
         const float alpha = !need ? 1.f : (st.m == -INFINITY ? 0.f : fast_exp2(-sh));
@@ -730,6 +733,7 @@ __device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, u
             sn[r] -= sh;
         }
         if (need) st.m = (st.m == -INFINITY ? 0.f : st.m) + sh;
+        st.thr = st.m == -INFINITY ? -INFINITY : 8.0f;
         const float nr = st.m == -INFINITY ? 0.f : -st.m;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.negr[r] = nr;
@@ -861,10 +865,13 @@ __device__ __forceinline__ void pipe_step(const PipeSrc &ps, int sidx, bool comp
         // the prefix tail: its first klim (< 64) keys; a tree stage: the
         // lane's ancestor-or-self bits
         const bool masked = sidx >= nfull;
-        const int klim = ps.kend - (ps.kbeg + sidx * kBN);
-        const int wi = sidx - ps.npre;
-        const uint64_t tw = wi <= 0 ? tw0 : wi == 1 ? tw1 : wi == 2 ? tw2 : tw3;
-        const uint64_t vis = !masked ? 0ull : sidx < ps.npre ? (1ull << klim) - 1ull : tw;
+        uint64_t vis = 0ull;
+        if (masked) {   // the same in every lane
+            const int klim = ps.kend - (ps.kbeg + sidx * kBN);
+            const int wi = sidx - ps.npre;
+            const uint64_t tw = wi <= 0 ? tw0 : wi == 1 ? tw1 : wi == 2 ? tw2 : tw3;
+            vis = sidx < ps.npre ? (1ull << klim) - 1ull : tw;
+        }
         pipe_stage<B>(sc, sn, qf, o, st, pl, h, masked, vis);
     }
     pipe_wait_stage();
@@ -923,7 +930,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave, 1) void tree_attn_pipe_kernel(Att
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-    RowState st{-INFINITY, 0.f, f32x16{}};
+    RowState st{-INFINITY, 0.f, f32x16{}, -INFINITY};
     f32x16 sc = f32x16{}, sn = f32x16{};
 
     // block 0 (first 32 keys of stage 0) before the pipeline starts
