@@ -67,6 +67,16 @@ __device__ __forceinline__ float chunk_elem<bf16_t>(const u32x4 &c, int e) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// Pointer types of the direct global-to-LDS loads (global_load_lds_dwordx4:
+// lane i's 16 bytes land at the wave-uniform LDS address + 16 i).
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) const void *gbl_ptr_t;
+
+// Streaming (non-temporal) load, for data read once: whole 128 B lines per
+// instruction stream faster this way; half lines per instruction do not.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // Buffer resource over [base, base + nbytes): raw buffer loads at byte
 // offsets >= nbytes return zero (hardware range check), so tails need no

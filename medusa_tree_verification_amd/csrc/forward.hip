@@ -371,9 +371,6 @@ constexpr int kBigTile = 256;
 constexpr int kBigMinRows = 256;
 constexpr int kBigSK = 64;          // k per stage (two k-steps of 32)
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef __attribute__((address_space(1))) const void *gbl_ptr_t;
-
 // s_waitcnt immediates: vmcnt(0) and vmcnt(16), lgkmcnt and expcnt untouched.
 // They count every vector-memory operation of the wave, so gemm_big_kernel
 // may issue none but its stage loads before its last barrier

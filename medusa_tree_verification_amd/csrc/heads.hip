@@ -16,17 +16,24 @@
 //   tiles); four waves split the d reduction; LDS sum; epilogue
 //   z = SiLU(u) + h written to the workspace (bf16 rounding once, in bf16
 //   mode).
-// Stage 2: the K*ceil(V/16) row tiles of W2 are split evenly over one
-//   workgroup of four waves per CU (measured: more concurrent waves streaming
-//   16-row tiles lose HBM efficiency).  Each wave streams up to four tiles at
-//   a time in batches of 8 k-steps (32 KB of loads in flight, issued ahead of
-//   the MFMAs), starting at a per-wave rotated batch so that lockstep waves
-//   hit different HBM channels; it keeps a per-lane top-s list of its column,
-//   merges lists across lanes (shuffles) and waves (LDS), and writes one
-//   partial list per (head, sequence) for its workgroup.  A small merge
-//   kernel (one workgroup per head) then reduces each head's partial lists
-//   into topk_ids / topk_vals: cheaper than having the last workgroup of a
-//   head merge them, whose device-scope fences cost more than a launch.
+// Stage 2: the row tiles of W2 (all heads' rows in one sequence) are split
+//   evenly over one workgroup of four waves per CU; each wave streams a
+//   contiguous range of them, in batches of 8 k-steps whose loads are issued
+//   ahead of the MFMAs, starting at a per-wave rotated batch so that lockstep
+//   waves hit different HBM channels.  Up to 8 sequences (with rows of 1 to
+//   8 KiB) the tiles have 8 rows and each load instruction fetches whole
+//   128 B lines (8 rows x 128 B, non-temporal): the MFMA's second half of
+//   rows and columns takes the second half of each line, and the B operand
+//   (z, at most two heads per workgroup) sits in LDS, filled by direct loads
+//   at the start.  Measured, this streams W2 at about 7 TB/s where 16-row
+//   tiles (16 rows x 64 B per load, kept for 9 to 16 sequences) reach about
+//   6.3; more rows in flight per wave, more waves per CU or non-temporal
+//   half-line loads were all slower.  Each wave keeps a per-lane top-s list
+//   of its column, merges lists across lanes (shuffles) and waves (LDS), and
+//   writes one partial list per (head, sequence) for its workgroup.  A small
+//   merge kernel (one workgroup per head) then reduces each head's partial
+//   lists into topk_ids / topk_vals: cheaper than having the last workgroup
+//   of a head merge them, whose device-scope fences cost more than a launch.
 #include "common.h"
 
 #include <mutex>
@@ -41,10 +48,12 @@ constexpr int kS2Waves = 4;              // stage 2: waves per workgroup
 constexpr int kS2Tiles = 4;              // stage 2: row tiles per wave pass
 constexpr int kS2Unroll = 8;             // stage 2: k-steps per batch of loads
 constexpr int kS2MaxWG = kNumCU;         // stage 2: workgroups (one per CU)
+constexpr int kS2ZSteps = 64;            // stage 2, 8-row tiles: 128 B steps of z held in LDS per head
 
 struct HeadsLayout {
     size_t z_off, part_off, total;
     int nh, ntph, nt, P;   // nh: streamed heads (K, plus the LM head when it rides along)
+    int tr;                // stage 2 tile rows: 8 (B <= 8, z in LDS) or 16
 };
 
 inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
@@ -52,7 +61,11 @@ inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
 inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype, int lm = 1) {
     HeadsLayout L;
     L.nh = K + (lm ? 1 : 0);
-    L.ntph = (V + 15) / 16;
+    // 8-row tiles when z of two heads fits in LDS (d * esize <= 128 B * kS2ZSteps)
+    // and a row holds a full batch of loads (1 KiB)
+    const size_t row_bytes = (size_t)d * esize(dtype);
+    L.tr = B <= 8 && row_bytes >= 128u * kS2Unroll && row_bytes <= 128u * kS2ZSteps ? 8 : 16;
+    L.ntph = (V + L.tr - 1) / L.tr;
     L.nt = L.nh * L.ntph;
     L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
     L.z_off = 0;
@@ -262,6 +275,51 @@ __device__ __forceinline__ void stream_tiles(f32x4 (&acc)[kS2Tiles], const T *__
     }
 }
 
+// acc += one 8-row W2 tile x z (up to 8 columns), over the full d.  Each
+// load covers whole 128 B lines: lane (c, g) holds row c % 8 at chunk
+// 4 * (c / 8) + g (16 B chunks) of every 128 B step, and its B operand is
+// column c % 8 of z at the same chunk, read from LDS where zl[step * 64] is
+// this lane's (stored in lane order: linear, conflict-free reads).  The
+// MFMA's rows and columns 0..7 then take the first half of each step and rows
+// and columns 8..15 the second, so C[i][j] + C[i + 8][j + 8] is the dot
+// product of row i and column j.  Batches, rotation and the tail as in
+// stream_tiles (at least one full batch: d * sizeof(T) >= 1 KiB); the weights
+// are read once, so they are streamed (non-temporal loads).  The caller has
+// issued the first batch into `a` (first_batch8), ahead of other work.
+template <typename T>
+__device__ __forceinline__ void load_batch8(u32x4 (&a)[kS2Unroll], const T *__restrict__ arow) {
+    constexpr int KSTEP = 8 * Elem<T>::kPer16B;
+#pragma unroll
+    for (int u = 0; u < kS2Unroll; ++u) a[u] = ld16_nt(arow + u * KSTEP);
+}
+template <typename T>
+__device__ __forceinline__ void mma_batch8(f32x4 &acc, const u32x4 (&a)[kS2Unroll], const u32x4 *zl) {
+    u32x4 b[kS2Unroll];
+#pragma unroll
+    for (int u = 0; u < kS2Unroll; ++u) b[u] = zl[u * kWave];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kS2Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
+}
+template <typename T>
+__device__ __forceinline__ void stream_tile8(f32x4 &acc, const T *__restrict__ arow,
+                                             const u32x4 *zl, int d, int rot,
+                                             u32x4 (&a)[kS2Unroll]) {
+    constexpr int KC = Elem<T>::kPer16B;
+    constexpr int KSTEP = 8 * KC;   // elements per 128 B step
+    constexpr int KB = KSTEP * kS2Unroll;
+    const int nb = d / KB;
+    int bi = rot % nb;
+    mma_batch8<T>(acc, a, zl + bi * kS2Unroll * kWave);
+    for (int i = 1; i < nb; ++i) {
+        bi = bi + 1 == nb ? 0 : bi + 1;
+        load_batch8<T>(a, arow + bi * KB);
+        mma_batch8<T>(acc, a, zl + bi * kS2Unroll * kWave);
+    }
+    for (int k0 = nb * KB; k0 < d; k0 += KSTEP)
+        mma16_step(acc, ld16_nt(arow + k0), zl[k0 / KSTEP * kWave], T{});
+}
+
 // Merge the partial top-s lists of head `head` (one per workgroup owning a
 // tile of it) into topk_ids / topk_vals: wave `wave` of workgroup row
 // blockIdx.y takes column blockIdx.y * kS2Waves + wave.
@@ -316,7 +374,29 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
 
 // LM: the LM head rides along as head K (a separate instantiation, so the
 // plain and the root-token streams show up as different kernels in traces).
-template <typename T, bool LM, int SM>
+// The row of 8-row tile `tile_in_head` that lane (c, g) streams, at its chunk.
+template <typename T>
+__device__ __forceinline__ const T *tile8_row(const T *wbase, int tile_in_head, int V, int d,
+                                              int c, int g) {
+    constexpr int KC = Elem<T>::kPer16B;
+    const int r = tile_in_head * 8 + c % 8;
+    return wbase + (size_t)(r < V ? r : V - 1) * d + (c / 8) * 4 * KC + g * KC;
+}
+
+// Issue the first batch (batch rot % nb) of 8-row tile t of the streamed
+// heads (head K, when LM: the LM head) into a.
+template <typename T, bool LM>
+__device__ __forceinline__ void first_batch8(u32x4 (&a)[kS2Unroll], const T *__restrict__ w2,
+                                             const T *__restrict__ w_lm, int t, int K, int V,
+                                             int d, int ntph, int c, int g, int rot) {
+    constexpr int KB = 8 * Elem<T>::kPer16B * kS2Unroll;
+    const int h = t / ntph;
+    const T *wb = LM && h == K ? w_lm : w2 + (size_t)h * V * d;
+    load_batch8<T>(a, tile8_row<T>(wb, t - h * ntph, V, d, c, g) + rot % (d / KB) * KB);
+}
+
+// TR: tile rows, 16 (stream_tiles, any B) or 8 (stream_tile8, B <= 8).
+template <typename T, bool LM, int SM, int TR>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, const T *__restrict__ w_lm,
     const T *__restrict__ hidden, float *__restrict__ logits_out, float2 *__restrict__ part, int B,
@@ -324,6 +404,9 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     constexpr int KC = Elem<T>::kPer16B;
     // per-wave merged lists: [wave][head slot 0/1][column][s]
     __shared__ float2 stage[kS2Waves][2][16][kSMax];
+    // 8-row tiles: the B operand of the workgroup's (at most two) heads,
+    // [head slot][128 B step][lane]
+    __shared__ u32x4 zl[TR == 8 ? 2 : 1][TR == 8 ? kS2ZSteps : 1][kWave];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int g = lane / 16, c = lane % 16;
@@ -339,6 +422,27 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     int tile = (int)(wg_beg + span * wv / kS2Waves);
     const int wend = (int)(wg_beg + span * (wv + 1) / kS2Waves);
     const int rot = (int)(((unsigned)wg * kS2Waves + wv) * 7u);
+    // 8-row tiles: the first batch of each tile is issued ahead, that of the
+    // wave's first tile before the z fill (whose loads then wait alongside
+    // it), that of the next tile before a tile's epilogue
+    u32x4 apre[kS2Unroll];
+    if constexpr (TR == 8) {
+        if (tile < wend) first_batch8<T, LM>(apre, w2, w_lm, tile, K, V, d, ntph, c, g, rot);
+        // z chunks in lane order: entry [slot][t][q] is what lane q = 16g + c
+        // multiplies in step t (column c % 8, chunk 4 * (c / 8) + g); each
+        // entry row is one direct-to-LDS load of a wave, all in flight at once
+        const int nstep = d / (8 * KC);
+        const int head_last = (int)((wg_end - 1) / ntph);
+        const int nslot = head_last - head_lo + 1;
+        const int col = c % 8 < B ? c % 8 : B - 1;
+        for (int e = wv; e < nslot * nstep; e += kS2Waves) {
+            const int slot = e / nstep, t = e % nstep, hd = head_lo + slot;
+            const T *src = LM && hd == K ? hidden + (size_t)col * d : z + ((size_t)col * K + hd) * d;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + t * 8 * KC + (c / 8) * 4 * KC + g * KC),
+                                             (lds_ptr_t)&zl[slot][t][0], 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the LDS writes have landed
+    }
     __syncthreads();
 
     const bool bcol = c < B;
@@ -362,6 +466,36 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
             L.clear();
             cur_head = head;
         }
+        const bool lmh = LM && head == K;   // head K (when streamed): the LM head on the hidden state
+        if constexpr (TR == 8) {
+            const int tile_in_head = tile - head * ntph;
+            const T *arow = tile8_row<T>(lmh ? w_lm : w2 + (size_t)head * V * d, tile_in_head, V, d, c, g);
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            stream_tile8<T>(acc, arow, &zl[TR == 8 ? head - head_lo : 0][0][lane], d, rot, apre);
+            if (tile + 1 < wend) first_batch8<T, LM>(apre, w2, w_lm, tile + 1, K, V, d, ntph, c, g, rot);
+            // lane 16g + j (g < 2, j < 8) holds C[4g + i][j], lane 16g + j + 40 C[4g + i + 8][j + 8]
+            f32x4 full;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) full[i] = acc[i] + __shfl(acc[i], lane + 40);
+            const int v0 = tile_in_head * 8 + 4 * g;
+            if (g < 2 && c < B) {
+                if (logits_out && head < K) {
+                    float *dst = logits_out + ((size_t)c * K + head) * V + v0;
+                    if (v0 + 3 < V && ((V & 3) == 0)) {
+                        *reinterpret_cast<f32x4 *>(dst) = full;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (v0 + i < V) dst[i] = full[i];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v0 + i < V) L.insert(full[i], v0 + i, s);
+            }
+            tile += 1;
+            continue;
+        }
         const int head_end = (head + 1) * ntph;
         const int gend = tile + kS2Tiles < wend ? tile + kS2Tiles : wend;
         const int n = __builtin_amdgcn_readfirstlane((gend < head_end ? gend : head_end) - tile);
@@ -370,9 +504,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
         f32x4 acc[kS2Tiles];
 #pragma unroll
         for (int r = 0; r < kS2Tiles; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // head K (when streamed) is the LM head: weights w_lm, input the hidden state
         const int bc = bcol ? c : B - 1;
-        const bool lmh = LM && head == K;
         const T *brow = lmh ? hidden + (size_t)bc * d + g * KC
                             : z + ((size_t)bc * K + head) * d + g * KC;
         const T *wbase = lmh ? w_lm + g * KC : w2 + (size_t)head * V * d + g * KC;
@@ -508,6 +640,15 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
+template <typename T>
+auto stage2_kernel(bool lm, bool s4, int tr) {
+    if (tr == 8)
+        return lm ? (s4 ? heads_stage2_kernel<T, true, 4, 8> : heads_stage2_kernel<T, true, kSMax, 8>)
+                  : (s4 ? heads_stage2_kernel<T, false, 4, 8> : heads_stage2_kernel<T, false, kSMax, 8>);
+    return lm ? (s4 ? heads_stage2_kernel<T, true, 4, 16> : heads_stage2_kernel<T, true, kSMax, 16>)
+              : (s4 ? heads_stage2_kernel<T, false, 4, 16> : heads_stage2_kernel<T, false, kSMax, 16>);
+}
+
 // The W2 stream with the fused per-workgroup top-s (partials into the
 // workspace).  w_lm == NULL: the K Medusa heads only; otherwise the LM head
 // (input: the hidden state) is streamed as head K.
@@ -522,15 +663,13 @@ int launch_stage2_stream(const void *w2, const void *w_lm, const void *hidden, i
     // lists of 4 when s <= 4 (every insert costs its capacity)
     const bool s4 = s <= 4;
     if (dtype == MEDUSA_BF16) {
-        auto *kern = lm ? (s4 ? heads_stage2_kernel<bf16_t, true, 4> : heads_stage2_kernel<bf16_t, true, kSMax>)
-                        : (s4 ? heads_stage2_kernel<bf16_t, false, 4> : heads_stage2_kernel<bf16_t, false, kSMax>);
+        auto *kern = stage2_kernel<bf16_t>(lm, s4, L.tr);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)w2,
                            (const bf16_t *)(base + L.z_off), (const bf16_t *)w_lm,
                            (const bf16_t *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
                            L.P);
     } else {
-        auto *kern = lm ? (s4 ? heads_stage2_kernel<float, true, 4> : heads_stage2_kernel<float, true, kSMax>)
-                        : (s4 ? heads_stage2_kernel<float, false, 4> : heads_stage2_kernel<float, false, kSMax>);
+        auto *kern = stage2_kernel<float>(lm, s4, L.tr);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)w2,
                            (const float *)(base + L.z_off), (const float *)w_lm,
                            (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
