@@ -24,11 +24,11 @@ extern "C" {
  * thread, so that no load or product can be optimised away). */
 size_t medusa_probe_sink_bytes(void);
 
-/* One linear pass of 16-byte loads over buf (device, 16-byte aligned,
- * bytes > 0 a multiple of 16): every byte read once; one workgroup of 1024
- * threads per CU streams its contiguous share with 4 loads in flight per
- * thread.  Time it with events; bytes / time is the streaming read
- * bandwidth. */
+/* One linear pass of 16-byte non-temporal loads over buf (device, 16-byte
+ * aligned, bytes > 0 a multiple of 16): every byte read once; one workgroup
+ * of four waves per CU streams its contiguous share with 8 loads in flight
+ * per thread (whole 128-byte lines per load).  Time it with events; bytes /
+ * time is the streaming read bandwidth. */
 int medusa_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
 
 /* 256 workgroups of four waves (one per SIMD), each wave running eight

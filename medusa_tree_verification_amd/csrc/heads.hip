@@ -53,7 +53,9 @@ constexpr int kS2ZSteps = 64;            // stage 2, 8-row tiles: 128 B steps of
 struct HeadsLayout {
     size_t z_off, part_off, total;
     int nh, ntph, nt, P;   // nh: streamed heads (K, plus the LM head when it rides along)
-    int tr;                // stage 2 tile rows: 8 (B <= 8, z in LDS) or 16
+    int tr;                // stage 2 tile rows: 8 (z in LDS) or 16
+    int cg;                // 8-row tiles: column groups of 8 sequences (1 or 2)
+    int G;                 // workgroups per head (cg == 2: one head each), else 0
 };
 
 inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
@@ -61,13 +63,23 @@ inline int esize(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
 inline HeadsLayout heads_layout(int B, int K, int d, int V, int dtype, int lm = 1) {
     HeadsLayout L;
     L.nh = K + (lm ? 1 : 0);
-    // 8-row tiles when z of two heads fits in LDS (d * esize <= 128 B * kS2ZSteps)
-    // and a row holds a full batch of loads (1 KiB)
+    // 8-row tiles when a row holds a full batch of loads (1 KiB) and z fits
+    // in LDS (d * esize <= 128 B * kS2ZSteps): up to 8 sequences, z of the
+    // (at most two) heads a workgroup spans; 9 to 16, z of one head in two
+    // column groups, so the workgroups are dealt out G per head
     const size_t row_bytes = (size_t)d * esize(dtype);
-    L.tr = B <= 8 && row_bytes >= 128u * kS2Unroll && row_bytes <= 128u * kS2ZSteps ? 8 : 16;
+    L.tr = row_bytes >= 128u * kS2Unroll && row_bytes <= 128u * kS2ZSteps ? 8 : 16;
+    L.cg = L.tr == 8 && B > 8 ? 2 : 1;
     L.ntph = (V + L.tr - 1) / L.tr;
     L.nt = L.nh * L.ntph;
-    L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
+    if (L.cg == 2) {
+        L.G = kS2MaxWG / L.nh < L.ntph ? kS2MaxWG / L.nh : L.ntph;
+        if (L.G < 1) L.G = 1;
+        L.P = L.G * L.nh;
+    } else {
+        L.G = 0;
+        L.P = L.nt < kS2MaxWG ? L.nt : kS2MaxWG;
+    }
     L.z_off = 0;
     L.part_off = align_up((size_t)B * K * d * esize(dtype), 256);
     L.total = L.part_off + align_up((size_t)L.nh * B * L.P * kSMax * 2 * sizeof(float), 256);
@@ -292,17 +304,24 @@ __device__ __forceinline__ void load_batch8(u32x4 (&a)[kS2Unroll], const T *__re
 #pragma unroll
     for (int u = 0; u < kS2Unroll; ++u) a[u] = ld16_nt(arow + u * KSTEP);
 }
-template <typename T>
-__device__ __forceinline__ void mma_batch8(f32x4 &acc, const u32x4 (&a)[kS2Unroll], const u32x4 *zl) {
-    u32x4 b[kS2Unroll];
+// CG column groups: acc[q] takes columns 8q..8q+7, whose B operands sit
+// kS2ZSteps * kWave entries apart in LDS (each weight load feeds CG MFMAs).
+template <typename T, int CG>
+__device__ __forceinline__ void mma_batch8(f32x4 (&acc)[CG], const u32x4 (&a)[kS2Unroll],
+                                           const u32x4 *zl) {
+    u32x4 b[CG][kS2Unroll];
 #pragma unroll
-    for (int u = 0; u < kS2Unroll; ++u) b[u] = zl[u * kWave];
+    for (int q = 0; q < CG; ++q)
+#pragma unroll
+        for (int u = 0; u < kS2Unroll; ++u) b[q][u] = zl[q * kS2ZSteps * kWave + u * kWave];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kS2Unroll; ++u) mma16_step(acc, a[u], b[u], T{});
+    for (int u = 0; u < kS2Unroll; ++u)
+#pragma unroll
+        for (int q = 0; q < CG; ++q) mma16_step(acc[q], a[u], b[q][u], T{});
 }
-template <typename T>
-__device__ __forceinline__ void stream_tile8(f32x4 &acc, const T *__restrict__ arow,
+template <typename T, int CG>
+__device__ __forceinline__ void stream_tile8(f32x4 (&acc)[CG], const T *__restrict__ arow,
                                              const u32x4 *zl, int d, int rot,
                                              u32x4 (&a)[kS2Unroll]) {
     constexpr int KC = Elem<T>::kPer16B;
@@ -310,14 +329,33 @@ __device__ __forceinline__ void stream_tile8(f32x4 &acc, const T *__restrict__ a
     constexpr int KB = KSTEP * kS2Unroll;
     const int nb = d / KB;
     int bi = rot % nb;
-    mma_batch8<T>(acc, a, zl + bi * kS2Unroll * kWave);
+    mma_batch8<T, CG>(acc, a, zl + bi * kS2Unroll * kWave);
     for (int i = 1; i < nb; ++i) {
         bi = bi + 1 == nb ? 0 : bi + 1;
         load_batch8<T>(a, arow + bi * KB);
-        mma_batch8<T>(acc, a, zl + bi * kS2Unroll * kWave);
+        mma_batch8<T, CG>(acc, a, zl + bi * kS2Unroll * kWave);
     }
-    for (int k0 = nb * KB; k0 < d; k0 += KSTEP)
-        mma16_step(acc, ld16_nt(arow + k0), zl[k0 / KSTEP * kWave], T{});
+    for (int k0 = nb * KB; k0 < d; k0 += KSTEP) {
+        const u32x4 w = ld16_nt(arow + k0);
+#pragma unroll
+        for (int q = 0; q < CG; ++q)
+            mma16_step(acc[q], w, zl[q * kS2ZSteps * kWave + k0 / KSTEP * kWave], T{});
+    }
+}
+
+// Workgroups of the stream: with G > 0, G per head (each owns a contiguous
+// range of that head's tiles); otherwise the nt tiles are dealt out evenly
+// over P workgroups in order, and tile t belongs to workgroup tile_wg(t).
+__device__ __forceinline__ int tile_wg(long long t, int nt, int P) {
+    return (int)(((t + 1) * P - 1) / nt);
+}
+// the first workgroup owning a tile of head `head`, and how many own one
+__device__ __forceinline__ int head_wg_first(int head, int ntph, int nt, int P, int G) {
+    return G > 0 ? head * G : tile_wg((long long)head * ntph, nt, P);
+}
+__device__ __forceinline__ int head_wg_count(int head, int ntph, int nt, int P, int G) {
+    return G > 0 ? G
+                 : tile_wg((long long)head * ntph + ntph - 1, nt, P) - tile_wg((long long)head * ntph, nt, P) + 1;
 }
 
 // Merge the partial top-s lists of head `head` (one per workgroup owning a
@@ -329,12 +367,9 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
                                                  float *__restrict__ topk_vals,
                                                  int32_t *__restrict__ root_token,
                                                  float *__restrict__ root_val, int head, int B,
-                                                 int K, int s, int ntph, int nt, int P, int wave,
-                                                 int lane) {
-    const long long first_tile = (long long)head * ntph, last_tile = first_tile + ntph - 1;
-    const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
-    const int wg_last = (int)(((last_tile + 1) * P - 1) / nt);
-    const int nparts = wg_last - wg_first + 1;
+                                                 int K, int s, int ntph, int nt, int P, int G,
+                                                 int wave, int lane) {
+    const int nparts = head_wg_count(head, ntph, nt, P, G);
     const int col = (int)blockIdx.y * kS2Waves + wave;   // one wave per (head, column)
     if (col < B) {
         TopList<SM> M;
@@ -372,8 +407,6 @@ __device__ __forceinline__ void merge_head_lists(const float2 *__restrict__ part
     }
 }
 
-// LM: the LM head rides along as head K (a separate instantiation, so the
-// plain and the root-token streams show up as different kernels in traces).
 // The row of 8-row tile `tile_in_head` that lane (c, g) streams, at its chunk.
 template <typename T>
 __device__ __forceinline__ const T *tile8_row(const T *wbase, int tile_in_head, int V, int d,
@@ -395,17 +428,41 @@ __device__ __forceinline__ void first_batch8(u32x4 (&a)[kS2Unroll], const T *__r
     load_batch8<T>(a, tile8_row<T>(wb, t - h * ntph, V, d, c, g) + rot % (d / KB) * KB);
 }
 
-// TR: tile rows, 16 (stream_tiles, any B) or 8 (stream_tile8, B <= 8).
-template <typename T, bool LM, int SM, int TR>
+// A wave's lists of one head into its stage slot (st[column][entry]):
+// merged over the four lanes of each column, written by lane group 0.
+template <int SM, int TR, int CG>
+__device__ __forceinline__ void flush_lists(TopList<SM> (&L)[CG], float2 (*st)[kSMax], int s,
+                                            int g, int c) {
+#pragma unroll
+    for (int q = 0; q < CG; ++q) {
+        float ov[kSMax];
+        int oi[kSMax];
+        group_merge(L[q], s, 16, ov, oi);
+        if (g == 0 && (TR == 16 || c < 8)) {
+#pragma unroll
+            for (int r = 0; r < kSMax; ++r)
+                if (r < s) st[q * 8 + c][r] = make_float2(ov[r], __int_as_float(oi[r]));
+        }
+        L[q].clear();
+    }
+}
+
+// LM: the LM head rides along as head K (a separate instantiation, so the
+// plain and the root-token streams show up as different kernels in traces).
+// TR: tile rows, 16 (stream_tiles, any B) or 8 (stream_tile8); CG (8-row
+// tiles): column groups, 1 for up to 8 sequences, 2 for 9 to 16 (then G > 0:
+// each workgroup within one head).
+template <typename T, bool LM, int SM, int TR, int CG>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     const T *__restrict__ w2, const T *__restrict__ z, const T *__restrict__ w_lm,
     const T *__restrict__ hidden, float *__restrict__ logits_out, float2 *__restrict__ part, int B,
-    int K, int d, int V, int s, int ntph, int nt, int P) {
+    int K, int d, int V, int s, int ntph, int nt, int P, int G) {
     constexpr int KC = Elem<T>::kPer16B;
     // per-wave merged lists: [wave][head slot 0/1][column][s]
     __shared__ float2 stage[kS2Waves][2][16][kSMax];
-    // 8-row tiles: the B operand of the workgroup's (at most two) heads,
-    // [head slot][128 B step][lane]
+    // 8-row tiles: the B operand, [slot][128 B step][lane]; a slot holds z of
+    // one of the workgroup's (at most two) heads (CG 1) or one column group
+    // of its one head (CG 2)
     __shared__ u32x4 zl[TR == 8 ? 2 : 1][TR == 8 ? kS2ZSteps : 1][kWave];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -415,7 +472,15 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     for (int i = threadIdx.x; i < kS2Waves * 2 * 16 * kSMax; i += blockDim.x)
         (&stage[0][0][0][0])[i] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
 
-    const long long wg_beg = (long long)wg * nt / P, wg_end = (long long)(wg + 1) * nt / P;
+    long long wg_beg, wg_end;
+    if (G > 0) {
+        const int h = wg / G, j = wg % G;
+        wg_beg = (long long)h * ntph + (long long)j * ntph / G;
+        wg_end = (long long)h * ntph + (long long)(j + 1) * ntph / G;
+    } else {
+        wg_beg = (long long)wg * nt / P;
+        wg_end = (long long)(wg + 1) * nt / P;
+    }
     const int head_lo = (int)(wg_beg / ntph);
     const long long span = wg_end - wg_beg;
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
@@ -429,14 +494,16 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     if constexpr (TR == 8) {
         if (tile < wend) first_batch8<T, LM>(apre, w2, w_lm, tile, K, V, d, ntph, c, g, rot);
         // z chunks in lane order: entry [slot][t][q] is what lane q = 16g + c
-        // multiplies in step t (column c % 8, chunk 4 * (c / 8) + g); each
-        // entry row is one direct-to-LDS load of a wave, all in flight at once
+        // multiplies in step t (column c % 8 of its group, chunk
+        // 4 * (c / 8) + g); each entry row is one direct-to-LDS load of a
+        // wave, all in flight at once
         const int nstep = d / (8 * KC);
         const int head_last = (int)((wg_end - 1) / ntph);
-        const int nslot = head_last - head_lo + 1;
-        const int col = c % 8 < B ? c % 8 : B - 1;
+        const int nslot = CG == 2 ? 2 : head_last - head_lo + 1;
         for (int e = wv; e < nslot * nstep; e += kS2Waves) {
-            const int slot = e / nstep, t = e % nstep, hd = head_lo + slot;
+            const int slot = e / nstep, t = e % nstep, hd = CG == 2 ? head_lo : head_lo + slot;
+            const int cc = (CG == 2 ? slot * 8 : 0) + c % 8;
+            const int col = cc < B ? cc : B - 1;
             const T *src = LM && hd == K ? hidden + (size_t)col * d : z + ((size_t)col * K + hd) * d;
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + t * 8 * KC + (c / 8) * 4 * KC + g * KC),
                                              (lds_ptr_t)&zl[slot][t][0], 16, 0, 0);
@@ -446,52 +513,51 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
     __syncthreads();
 
     const bool bcol = c < B;
-    TopList<SM> L;
-    L.clear();
+    // per-lane lists: column c (16-row tiles), columns 8q + c (8-row tiles,
+    // lanes c < 8; the other lanes' lists stay empty)
+    TopList<SM> L[CG];
+#pragma unroll
+    for (int q = 0; q < CG; ++q) L[q].clear();
     int cur_head = tile < wend ? tile / ntph : -1;
 
     while (tile < wend) {
         const int head = tile / ntph;
         if (head != cur_head) {
-            // flush the finished head's lists
-            float ov[kSMax];
-            int oi[kSMax];
-            group_merge(L, s, 16, ov, oi);
-            if (g == 0) {
-#pragma unroll
-                for (int r = 0; r < kSMax; ++r)
-                    if (r < s)
-                        stage[wave][cur_head - head_lo][c][r] = make_float2(ov[r], __int_as_float(oi[r]));
-            }
-            L.clear();
+            flush_lists<SM, TR, CG>(L, stage[wave][cur_head - head_lo], s, g, c);
             cur_head = head;
         }
         const bool lmh = LM && head == K;   // head K (when streamed): the LM head on the hidden state
         if constexpr (TR == 8) {
             const int tile_in_head = tile - head * ntph;
             const T *arow = tile8_row<T>(lmh ? w_lm : w2 + (size_t)head * V * d, tile_in_head, V, d, c, g);
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            stream_tile8<T>(acc, arow, &zl[TR == 8 ? head - head_lo : 0][0][lane], d, rot, apre);
+            f32x4 acc[CG];
+#pragma unroll
+            for (int q = 0; q < CG; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            stream_tile8<T, CG>(acc, arow, &zl[CG == 1 ? head - head_lo : 0][0][lane], d, rot, apre);
             if (tile + 1 < wend) first_batch8<T, LM>(apre, w2, w_lm, tile + 1, K, V, d, ntph, c, g, rot);
-            // lane 16g + j (g < 2, j < 8) holds C[4g + i][j], lane 16g + j + 40 C[4g + i + 8][j + 8]
-            f32x4 full;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) full[i] = acc[i] + __shfl(acc[i], lane + 40);
             const int v0 = tile_in_head * 8 + 4 * g;
-            if (g < 2 && c < B) {
-                if (logits_out && head < K) {
-                    float *dst = logits_out + ((size_t)c * K + head) * V + v0;
-                    if (v0 + 3 < V && ((V & 3) == 0)) {
-                        *reinterpret_cast<f32x4 *>(dst) = full;
-                    } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (v0 + i < V) dst[i] = full[i];
+            for (int q = 0; q < CG; ++q) {
+                // lane 16g + j (g < 2, j < 8) holds C[4g + i][j], lane 16g + j + 40 C[4g + i + 8][j + 8]
+                f32x4 full;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) full[i] = acc[q][i] + __shfl(acc[q][i], lane + 40);
+                const int col = q * 8 + c;
+                if (g < 2 && c < 8 && col < B) {
+                    if (logits_out && head < K) {
+                        float *dst = logits_out + ((size_t)col * K + head) * V + v0;
+                        if (v0 + 3 < V && ((V & 3) == 0)) {
+                            *reinterpret_cast<f32x4 *>(dst) = full;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (v0 + i < V) dst[i] = full[i];
+                        }
                     }
-                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (v0 + i < V) L.insert(full[i], v0 + i, s);
+                    for (int i = 0; i < 4; ++i)
+                        if (v0 + i < V) L[q].insert(full[i], v0 + i, s);
+                }
             }
             tile += 1;
             continue;
@@ -534,22 +600,12 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (v0 + i < V) L.insert(acc[r][i], v0 + i, s);
+                    if (v0 + i < V) L[0].insert(acc[r][i], v0 + i, s);
             }
         }
         tile += n;
     }
-    if (cur_head >= 0) {
-        float ov[kSMax];
-        int oi[kSMax];
-        group_merge(L, s, 16, ov, oi);
-        if (g == 0) {
-#pragma unroll
-            for (int r = 0; r < kSMax; ++r)
-                if (r < s)
-                    stage[wave][cur_head - head_lo][c][r] = make_float2(ov[r], __int_as_float(oi[r]));
-        }
-    }
+    if (cur_head >= 0) flush_lists<SM, TR, CG>(L, stage[wave][cur_head - head_lo], s, g, c);
     __syncthreads();
 
     // workgroup merge: one thread per (head slot, column)
@@ -559,10 +615,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
         const int slot = threadIdx.x / 16, col = threadIdx.x % 16;
         const int head = head_lo + slot;
         if (col < B) {
-            // first workgroup that owns a tile of this head
-            const long long first_tile = (long long)head * ntph;
-            const int wg_first = (int)(((first_tile + 1) * P - 1) / nt);
-            float2 *dst = part + (((size_t)head * B + col) * P + (wg - wg_first)) * kSMax;
+            float2 *dst = part + (((size_t)head * B + col) * P + (wg - head_wg_first(head, ntph, nt, P, G))) * kSMax;
             for (int r = 0; r < s; ++r) {
                 float bv = -INFINITY;
                 int bi = 0x7FFFFFFF, bw = -1, br = -1;
@@ -591,9 +644,9 @@ template <int SM>
 __global__ __launch_bounds__(kS2Waves *kWave) void heads_merge_kernel(
     const float2 *__restrict__ part, int32_t *__restrict__ topk_ids, float *__restrict__ topk_vals,
     int32_t *__restrict__ root_token, float *__restrict__ root_val, int B, int K, int s, int ntph,
-    int nt, int P) {
+    int nt, int P, int G) {
     merge_head_lists<SM>(part, topk_ids, topk_vals, root_token, root_val, (int)blockIdx.x, B, K, s,
-                     ntph, nt, P, (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
+                         ntph, nt, P, G, (int)(threadIdx.x / kWave), (int)(threadIdx.x % kWave));
 }
 
 // --------------------------------------------------------------- host side
@@ -640,13 +693,15 @@ int launch_stage1(const void *hidden, const void *w1, int B, int K, int d, int V
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 
+template <typename T, int TR, int CG>
+auto stage2_kernel_tr(bool lm, bool s4) {
+    return lm ? (s4 ? heads_stage2_kernel<T, true, 4, TR, CG> : heads_stage2_kernel<T, true, kSMax, TR, CG>)
+              : (s4 ? heads_stage2_kernel<T, false, 4, TR, CG> : heads_stage2_kernel<T, false, kSMax, TR, CG>);
+}
 template <typename T>
-auto stage2_kernel(bool lm, bool s4, int tr) {
-    if (tr == 8)
-        return lm ? (s4 ? heads_stage2_kernel<T, true, 4, 8> : heads_stage2_kernel<T, true, kSMax, 8>)
-                  : (s4 ? heads_stage2_kernel<T, false, 4, 8> : heads_stage2_kernel<T, false, kSMax, 8>);
-    return lm ? (s4 ? heads_stage2_kernel<T, true, 4, 16> : heads_stage2_kernel<T, true, kSMax, 16>)
-              : (s4 ? heads_stage2_kernel<T, false, 4, 16> : heads_stage2_kernel<T, false, kSMax, 16>);
+auto stage2_kernel(bool lm, bool s4, int tr, int cg) {
+    if (tr == 8) return cg == 2 ? stage2_kernel_tr<T, 8, 2>(lm, s4) : stage2_kernel_tr<T, 8, 1>(lm, s4);
+    return stage2_kernel_tr<T, 16, 1>(lm, s4);
 }
 
 // The W2 stream with the fused per-workgroup top-s (partials into the
@@ -663,17 +718,17 @@ int launch_stage2_stream(const void *w2, const void *w_lm, const void *hidden, i
     // lists of 4 when s <= 4 (every insert costs its capacity)
     const bool s4 = s <= 4;
     if (dtype == MEDUSA_BF16) {
-        auto *kern = stage2_kernel<bf16_t>(lm, s4, L.tr);
+        auto *kern = stage2_kernel<bf16_t>(lm, s4, L.tr, L.cg);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t *)w2,
                            (const bf16_t *)(base + L.z_off), (const bf16_t *)w_lm,
                            (const bf16_t *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
-                           L.P);
+                           L.P, L.G);
     } else {
-        auto *kern = stage2_kernel<float>(lm, s4, L.tr);
+        auto *kern = stage2_kernel<float>(lm, s4, L.tr, L.cg);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const float *)w2,
                            (const float *)(base + L.z_off), (const float *)w_lm,
                            (const float *)hidden, logits_out, part, B, K, d, V, s, L.ntph, L.nt,
-                           L.P);
+                           L.P, L.G);
     }
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
@@ -688,7 +743,7 @@ int launch_stage2_merge(bool lm, int B, int K, int d, int V, int s, int dtype, i
     hipLaunchKernelGGL(s <= 4 ? heads_merge_kernel<4> : heads_merge_kernel<kSMax>,
                        dim3((unsigned)L.nh, (unsigned)((B + kS2Waves - 1) / kS2Waves)),
                        dim3(kS2Waves * kWave), 0, st, part, topk_ids, topk_vals, root_token,
-                       root_val, B, K, s, L.ntph, L.nt, L.P);
+                       root_val, B, K, s, L.ntph, L.nt, L.P, L.G);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
 }
 

@@ -2,10 +2,12 @@
 // against, measured on the device itself (the published MI355X figures are
 // 8 TB/s of HBM3E and 2.5 PFLOP/s of dense bf16 MFMA).
 //
-//  - medusa_probe_read: a linear stream of 16-byte loads over a caller
-//    buffer (the access pattern of the weight and KV streams), every byte
-//    read once; the loaded words are folded into one value per thread so
-//    that no load can be dropped.
+//  - medusa_probe_read: a linear stream of 16-byte non-temporal loads over a
+//    caller buffer, every byte read once, four waves per CU with eight loads
+//    (8 KiB of whole 128 B lines per wave) in flight: the fastest read shape
+//    measured (plain loads, or sixteen waves per CU, stream about 15% slower);
+//    the loaded words are folded into one value per thread so that no load
+//    can be dropped.
 //  - medusa_probe_mfma: independent chains of v_mfma_f32_32x32x16_bf16 on
 //    register operands, four waves per CU (one per SIMD, eight accumulator
 //    chains each), no memory traffic in the loop.
@@ -15,16 +17,16 @@
 namespace medusa {
 namespace {
 
-constexpr int kProbeThreads = 1024;
-constexpr int kProbeU = 4;          // 16-byte loads in flight per thread
+constexpr int kProbeThreads = 256;
+constexpr int kProbeU = 8;          // 16-byte loads in flight per thread
 constexpr int kProbeWG = kNumCU;    // one workgroup per CU, each streaming its own share
 constexpr int kMfmaWaves = 4;       // one wave per SIMD ...
 constexpr int kMfmaChains = 8;      // ... with eight independent accumulator chains
 
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4 *__restrict__ src,
                                                                    size_t n16, uint32_t *sink) {
-    // workgroup w streams its contiguous share; a wave's U loads cover U
-    // consecutive kilobytes
+    // workgroup w streams its contiguous share; each of a wave's U loads
+    // covers one kilobyte
     const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
     const size_t lo = (size_t)blockIdx.x * per;
     const size_t hi = lo + per < n16 ? lo + per : n16;
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4 *
 #pragma unroll
         for (int u = 0; u < kProbeU; ++u) {
             const size_t i = i0 + (size_t)u * kProbeThreads;
-            v[u] = i < hi ? src[i] : u32x4{0u, 0u, 0u, 0u};
+            v[u] = i < hi ? ld16_nt(src + i) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kProbeU; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];

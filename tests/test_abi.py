@@ -49,7 +49,8 @@ def test_every_declared_symbol_is_exported(mv):
 
 def test_probe_validation(mv):
     L = mv.lib
-    assert L.medusa_probe_sink_bytes() >= 256 * 1024 * 4
+    # one word per thread: the read probe's 256 x 256 threads, the MFMA probe's 256 x 4 waves
+    assert L.medusa_probe_sink_bytes() >= max(256 * 256, 256 * 4 * 64) * 4
     assert L.medusa_probe_read(None, 16, FAKE, None) == -1
     assert L.medusa_probe_read(FAKE, 15, FAKE, None) == -2
     assert L.medusa_probe_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == -2

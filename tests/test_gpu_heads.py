@@ -66,6 +66,10 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05, s=None, w_lm_std=None):
     (4, 3, 512, 3001, 3),      # 8-row tiles (B <= 8): ragged last tile
     (8, 2, 1024, 20000, 4),    # 8-row tiles: all eight columns, many tiles per workgroup
     (1, 4, 640, 4099, 2),      # 8-row tiles: a batch and leftover steps per row
+    (12, 3, 512, 3001, 3),     # 8-row tiles, two column groups (the second partial)
+    (16, 2, 1024, 20000, 4),   # 8-row tiles, all sixteen columns, many tiles per workgroup
+    (9, 5, 640, 4099, 2),      # two column groups: one column in the second, leftover steps
+    (10, 2, 512, 100, 3),      # two column groups, fewer tiles per head than workgroups
 ])
 def test_heads_random_shapes(dtype, B, K, d, V, s):
     hx, ref, _ = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype, s=s)
@@ -167,7 +171,7 @@ def _root_check(out, lm, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,K,d,V,s", [(1, 1, 128, 16, 1), (3, 2, 384, 777, 8),
                                        (16, 5, 256, 4099, 3), (7, 4, 128, 70000, 3),
-                                       (4, 3, 512, 3001, 3)])
+                                       (4, 3, 512, 3001, 3), (12, 3, 512, 3001, 3)])
 def test_heads_root_random(dtype, B, K, d, V, s):
     seed = hash((B, K, d, V, s, 7)) % 10000 * 10
     hx, ref, lm = _random_heads(seed, B, K, d, V, dtype, s=s, w_lm_std=0.05)
