@@ -20,17 +20,20 @@
 //   evenly over one workgroup of four waves per CU; each wave streams a
 //   contiguous range of them, in batches of 8 k-steps whose loads are issued
 //   ahead of the MFMAs, starting at a per-wave rotated batch so that lockstep
-//   waves hit different HBM channels.  Up to 8 sequences (with rows of 1 to
-//   8 KiB) the tiles have 8 rows and each load instruction fetches whole
-//   128 B lines (8 rows x 128 B, non-temporal): the MFMA's second half of
-//   rows and columns takes the second half of each line, and the B operand
-//   (z, at most two heads per workgroup) sits in LDS, filled by direct loads
-//   at the start.  Measured, this streams W2 at about 7 TB/s where 16-row
-//   tiles (16 rows x 64 B per load, kept for 9 to 16 sequences) reach about
-//   6.3; more rows in flight per wave, more waves per CU or non-temporal
-//   half-line loads were all slower.  Each wave keeps a per-lane top-s list
-//   of its column, merges lists across lanes (shuffles) and waves (LDS), and
-//   writes one partial list per (head, sequence) for its workgroup.  A small
+//   waves hit different HBM channels.  With rows of 1 to 8 KiB the tiles
+//   have 8 rows and each load instruction fetches whole 128 B lines (8 rows
+//   x 128 B, non-temporal): the MFMA's second half of rows and columns takes
+//   the second half of each line, and the B operand (z) sits in LDS, filled
+//   by direct loads at the start: of the (at most two) heads a workgroup
+//   spans for up to 8 sequences; of one head in two column groups of 8 for 9
+//   to 16 (each workgroup then owns tiles of one head, and every weight load
+//   feeds two MFMAs).  Measured, this streams W2 at about 7 TB/s where
+//   16-row tiles (16 rows x 64 B per load, kept for other row lengths) reach
+//   about 6.3; more rows in flight per wave, more waves per CU or
+//   non-temporal half-line loads were all slower.  Each wave keeps per-lane
+//   top-s lists of its columns, merges lists across lanes (shuffles) and
+//   waves (LDS), and writes one partial list per (head, sequence) for its
+//   workgroup.  A small
 //   merge kernel (one workgroup per head) then reduces each head's partial
 //   lists into topk_ids / topk_vals: cheaper than having the last workgroup
 //   of a head merge them, whose device-scope fences cost more than a launch.
