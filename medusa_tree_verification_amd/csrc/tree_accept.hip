@@ -124,11 +124,11 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax *sh) {
 }
 
 // Argmax over 16-byte chunks: the best chunk's maximum and its first element
-// index; the element index is resolved once at the end by reading that
-// chunk again (an L2 hit), which costs fewer operations per chunk than
-// carrying its bits.  The first chunk is always taken; later ones only when
-// strictly larger, so on ties the earlier chunk, and within it the earlier
-// element, wins.
+// index.  The first chunk is always taken; later ones only when strictly
+// larger, so on ties the earlier chunk wins.  The element index is resolved
+// once per workgroup, after the block reduction has picked the winning chunk
+// (resolve_chunk: one thread reads that chunk again), which costs fewer
+// operations per chunk than carrying its bits.
 struct ChunkArgMax {
     float v;
     int base;      // element index of the chunk's first element; -1: none yet
@@ -137,19 +137,21 @@ struct ChunkArgMax {
         v = take ? cm : v;
         base = take ? b : base;
     }
-    // rs: the buffer resource the chunks were read through, starting at
-    // element lo of the row
-    template <typename T>
-    __device__ __forceinline__ void resolve(ArgMax &am, __amdgpu_buffer_rsrc_t rs, int lo) const {
-        if (base < 0) return;
-        constexpr int E = Elem<T>::kPer16B;
-        const u32x4 bits = buf_ld16(rs, (uint32_t)(base - lo) * (uint32_t)sizeof(T));
-        int e0 = E - 1;
-#pragma unroll
-        for (int e = E - 1; e >= 0; --e) e0 = chunk_elem<T>(bits, e) == v ? e : e0;
-        am.add(v, base + e0);
-    }
 };
+// r: the block's winning (chunk maximum, chunk start) of row; the first
+// element of that chunk equal to the maximum (within a chunk, the earlier
+// element wins ties, as across chunks).
+template <typename T>
+__device__ __forceinline__ ArgMax resolve_chunk(ArgMax r, const T *__restrict__ row) {
+    if (r.i == 0x7FFFFFFF) return r;
+    constexpr int E = Elem<T>::kPer16B;
+    const u32x4 bits = ld16(row + r.i);
+    int e0 = E - 1;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) e0 = chunk_elem<T>(bits, e) == r.v ? e : e0;
+    r.i += e0;
+    return r;
+}
 
 // One 16-byte chunk (E elements from index base): argmax, and (typical) the
 // softmax statistics of x * zs with one fused multiply-add per element.
@@ -199,13 +201,15 @@ __device__ __forceinline__ float buf_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, uint
 }
 
 // Raw argmax and (typical) softmax statistics of row[lo, hi), this thread's
-// share of the whole workgroup's pass.  Loads go through a buffer resource
+// share of the whole workgroup's pass.  Returns true when am is chunk-level
+// (index: the chunk's first element; resolve_chunk after the block
+// reduction), false when it is element-level.  Loads go through a buffer resource
 // over exactly [lo, hi), so they need no predicate (past the end they read 0)
 // and all U of them are in flight together; only the accumulation is
 // predicated.  16-byte loads need V % E == 0 (rows then start 16-byte
 // aligned) and E-aligned bounds; otherwise element loads.
 template <typename T, int U = kUnroll, int NT = kThreads>
-__device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int hi, int V,
+__device__ __forceinline__ bool row_stats(const T *__restrict__ row, int lo, int hi, int V,
                                           bool typical, float zs, ArgMax &am, SoftStats &st) {
     constexpr int E = Elem<T>::kPer16B;
     const auto rs = make_rsrc(row + lo, (uint32_t)(hi - lo) * (uint32_t)sizeof(T));
@@ -222,8 +226,10 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
                 if (ch < nch) add_chunk_fast<T>(c[u], lo + ch * E, typical, zs, cam, st);
             }
         }
-        cam.resolve<T>(am, rs, lo);
-    } else {
+        if (cam.base >= 0) am = ArgMax{cam.v, cam.base};
+        return true;
+    }
+    {
         const int n = hi - lo;
         for (int base = (int)threadIdx.x; base < n; base += U * NT) {
             float x[U];
@@ -239,6 +245,7 @@ __device__ __forceinline__ void row_stats(const T *__restrict__ row, int lo, int
             }
         }
     }
+    return false;
 }
 
 template <typename T>
@@ -261,14 +268,15 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams p) 
     ArgMax am{-INFINITY, 0x7FFFFFFF};
     SoftStats st{-INFINITY, 0.f, 0.f};
     const bool st_needed = typical && internal;   // softmax statistics: internal rows only
-    row_stats<T>(row, lo, hi, p.V, st_needed, p.zscale, am, st);
+    const bool chunked = row_stats<T>(row, lo, hi, p.V, st_needed, p.zscale, am, st);
     if ((int)threadIdx.x < p.T && c > 0 && cpar == n) {
         // the tokens of n's children, and (typical) each one's logit in this row
         if (j == 0) p.ctok[(size_t)b * p.T + c] = tok;
         if (typical && tok >= lo && tok < hi) p.childz[(size_t)b * p.T + c] = Elem<T>::to_f32(row[tok]);
     }
 
-    const ArgMax r = block_argmax<kThreads>(am, red);
+    ArgMax r = block_argmax<kThreads>(am, red);
+    if (chunked && threadIdx.x == 0) r = resolve_chunk<T>(r, row);
     if (st_needed) {
         for (int m = 32; m >= 1; m >>= 1) {
             const float m2 = __shfl_xor(st.m, m), S2 = __shfl_xor(st.S, m), A2 = __shfl_xor(st.A, m);
@@ -477,9 +485,9 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AcceptParams
     const T *row = (const T *)p.logits + ((size_t)b * p.T + best) * p.V;
     ArgMax am{-INFINITY, 0x7FFFFFFF};
     SoftStats unused{-INFINITY, 0.f, 0.f};
-    row_stats<T, kScanUnroll, kFinThreads>(row, 0, p.V, p.V, false, 0.f, am, unused);
+    const bool chunked = row_stats<T, kScanUnroll, kFinThreads>(row, 0, p.V, p.V, false, 0.f, am, unused);
     const ArgMax r = block_argmax<kFinThreads>(am, red);
-    if (tid == 0) p.next_token[b] = r.i;
+    if (tid == 0) p.next_token[b] = chunked ? resolve_chunk<T>(r, row).i : r.i;
 }
 
 // ---------------------------------------------------------------- bonus token
