@@ -1064,6 +1064,59 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(AttnParams p) {
     for (int e = 0; e < PER; ++e) dst[lane * PER + e] = Elem<T>::from_f32(acc[e] * inv);
 }
 
+// The same merge for up to kCombU splits with two rows per wave (lanes
+// 0-31 and 32-63), each lane holding DH / 32 elements of its row (16 bytes
+// of an fp32 partial per split at dh = 128): half the load instructions of
+// one row per wave.  One round of loads as above; the (max, sum) of a row's
+// split j sits in lane j of its half, and every reduction stays within the
+// half.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void tree_attn_combine2_kernel(AttnParams p) {
+    const int lane = threadIdx.x % kWave, hl = lane % 32, half = lane / 32;
+    const size_t nrows = (size_t)p.B * p.Hq * p.T;
+    const size_t row = ((size_t)blockIdx.x * 4 + threadIdx.x / kWave) * 2 + half;
+    const bool rv = row < nrows;
+    const size_t rid = rv ? row : nrows - 1;   // a missing second row: a copy, never stored
+    const int b = (int)(rid / ((size_t)p.Hq * p.T));
+    constexpr int PER = DH / 32;
+    const int j = hl < p.nsplit ? hl : 0;
+    const float2 ml = p.part_ml[(size_t)j * nrows + rid];
+    float v[kCombU][PER];
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+        if (u < p.nsplit) {   // the same in every lane; v[u] is read only for u < nsb
+            const float *src = p.part_o + ((size_t)u * nrows + rid) * DH + hl * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+        }
+    }
+    int L = p.prefix_len[b];
+    L = L < 0 ? 0 : (L > p.Lcap ? p.Lcap : L);
+    const int nsb = L > 0 ? (L + p.chunk - 1) / p.chunk : 1;   // at most nsplit
+    const bool live = hl < nsb;
+    float mmax = live ? ml.x : -INFINITY;
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, m));
+    const float w = live ? fast_exp2(ml.x - mmax) : 0.f;
+    float den = live ? w * ml.y : 0.f;
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) den += __shfl_xor(den, m);
+    float acc[PER] = {};
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+        const float wu = __shfl(w, half * 32 + u);
+        if (u < nsb) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wu * v[u][e];
+        }
+    }
+    if (!rv || nsb == 1) return;   // one split: the main kernel wrote the row
+    const float inv = 1.0f / den;
+    T *dst = (T *)p.out + rid * DH + hl * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = Elem<T>::from_f32(acc[e] * inv);
+}
+
 struct AttnPlan {
     int G, M, W, nmt, ks, nsplit, chunk, nwg;
     size_t err_off, o_off, ml_off, total;
@@ -1142,8 +1195,12 @@ int launch_attn(const AttnParams &p, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     if (p.nsplit > 1) {
         const size_t rows = (size_t)p.B * p.Hq * p.T;
-        hipLaunchKernelGGL((tree_attn_combine_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)),
-                           dim3(256), 0, st, p);
+        if (p.nsplit <= kCombU)
+            hipLaunchKernelGGL((tree_attn_combine2_kernel<T, DH>), dim3((unsigned)((rows + 7) / 8)),
+                               dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((tree_attn_combine_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)),
+                               dim3(256), 0, st, p);
         if (hipGetLastError() != hipSuccess) return MEDUSA_ERR_LAUNCH;
     }
     return MEDUSA_OK;
