@@ -268,3 +268,61 @@ def test_no_bit_cast_of_vector_elements():
             if re.search(r"__builtin_bit_cast\([^,]+,\s*[\w.]+\[[^\]]+\]\s*\)", line):
                 bad.append(f"{src}:{n}: {line.strip()}")
     assert not bad, bad
+
+
+def _mfma16(a_lanes, b_lanes):
+    """16x16 MFMA tile over one k-step as the hardware defines it: lane l
+    brings row l % 16 of A and column l % 16 of B, its elements covering lane
+    group l / 16's share of k; the result element r of lane l is
+    C[4 (l / 16) + r][l % 16]."""
+    C = np.zeros((16, 16))
+    for i in range(16):
+        for j in range(16):
+            C[i, j] = sum(float(np.dot(a_lanes[16 * g + i], b_lanes[16 * g + j])) for g in range(4))
+    return np.array([[C[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)])
+
+
+@pytest.mark.parametrize("kc,B,cg", [(8, 1, 1), (8, 8, 1), (4, 5, 1), (8, 16, 2), (8, 9, 2), (4, 12, 2)])
+def test_heads_rows8_layout(kc, B, cg):
+    """The 8-row stage-2 tile: lane (c, g) loads W row c % 8 at chunk
+    4 (c / 8) + g of each 128-byte step (kc elements per 16-byte chunk) and
+    reads its B operand from LDS entry [slot][step][lane], filled with column
+    8 slot + c % 8 (clamped to B - 1) of z at the same chunk; then for every
+    live lane (g < 2, c < 8, column 8 q + c < B) acc + acc of lane + 40 is the
+    dot product of tile row 4 g + r with that column over the whole row."""
+    rng = np.random.default_rng(11)
+    steps = 3
+    d = steps * 8 * kc
+    rows, tile = 21, 2                       # a ragged tile: rows 16..20 exist, 21..23 clamp
+    W = rng.standard_normal((rows, d))
+    z = rng.standard_normal((B, d))
+    # the LDS fill: entry [slot][t][q]
+    zl = np.zeros((cg, steps, 64, kc))
+    for slot in range(cg):
+        for t in range(steps):
+            for q in range(64):
+                cq = q % 16
+                col = min((slot * 8 if cg == 2 else 0) + cq % 8, B - 1)
+                off = t * 8 * kc + (cq // 8) * 4 * kc + (q // 16) * kc
+                zl[slot, t, q] = z[col, off:off + kc]
+    acc = np.zeros((cg, 64, 4))
+    for t in range(steps):
+        a_lanes = []
+        for lane in range(64):
+            c, g = lane % 16, lane // 16
+            r = min(tile * 8 + c % 8, rows - 1)
+            off = t * 8 * kc + (c // 8) * 4 * kc + g * kc
+            a_lanes.append(W[r, off:off + kc])
+        for q in range(cg):
+            acc[q] += _mfma16(a_lanes, [zl[q, t, lane] for lane in range(64)])
+    for q in range(cg):
+        for lane in range(64):
+            c, g = lane % 16, lane // 16
+            col = q * 8 + c
+            if not (g < 2 and c < 8 and col < B):
+                continue
+            for r in range(4):
+                v = tile * 8 + 4 * g + r
+                full = acc[q, lane, r] + acc[q, (lane + 40) % 64, r]
+                if v < rows:
+                    assert abs(full - float(np.dot(W[v], z[col]))) < 1e-9
