@@ -347,18 +347,60 @@ __device__ __forceinline__ void stream_tile8(f32x4 (&acc)[CG], const T *__restri
 }
 
 // Workgroups of the stream: with G > 0, G per head (each owns a contiguous
-// range of that head's tiles); otherwise the nt tiles are dealt out evenly
-// over P workgroups in order, and tile t belongs to workgroup tile_wg(t).
-__device__ __forceinline__ int tile_wg(long long t, int nt, int P) {
-    return (int)(((t + 1) * P - 1) / nt);
+// range of that head's tiles); otherwise the nt tiles are dealt out over P
+// workgroups in order, and tile t belongs to workgroup tile_wg(t).
+//
+// Workgroups are dispatched round-robin over the XCDs, so hardware id w runs
+// on XCD w mod 8, and the odd-numbered XCDs stream about 6% slower than the
+// even ones (measured on every box: per-wave end stamps, whichever part of
+// W2 they read).  So the shares are weighted: kXcdShare + 1 tiles' worth on
+// an even workgroup for every kXcdShare - 1 on an odd one, when every wave
+// gets kXcdMinTiles tiles or more.  With fewer the whole-tile rounding
+// decides (on 15-16 tiles per wave the slowest wave keeps its count and the
+// even XCDs only get more: llama7b_b1 stage 2 1.6 us slower, against 17 us
+// faster on large_vocab_typical's 78 tiles per wave).  share_prefix(j, base)
+// is the summed share of workgroups base .. base + j - 1.
+constexpr int kXcdShare = 32;
+constexpr int kXcdMinTiles = 32;
+__device__ __forceinline__ long long share_prefix(int j, int base, bool wt) {
+    if (!wt) return j;
+    return (long long)kXcdShare * j + ((j & 1) ? ((base & 1) ? -1 : 1) : 0);
+}
+__device__ __forceinline__ bool xcd_weighted(int ntph, int nt, int P, int G) {
+    return G > 0 ? ntph >= kXcdMinTiles * kS2Waves * G : nt >= kXcdMinTiles * kS2Waves * P;
+}
+// tiles [wg_beg, wg_end) of workgroup wg
+__device__ __forceinline__ void wg_tiles(int wg, int ntph, int nt, int P, int G, long long &beg,
+                                         long long &end) {
+    const bool wt = xcd_weighted(ntph, nt, P, G);
+    if (G > 0) {
+        const int h = wg / G, j = wg % G;
+        const long long D = share_prefix(G, h * G, wt);
+        beg = (long long)h * ntph + ntph * share_prefix(j, h * G, wt) / D;
+        end = (long long)h * ntph + ntph * share_prefix(j + 1, h * G, wt) / D;
+    } else {
+        const long long D = share_prefix(P, 0, wt);
+        beg = nt * share_prefix(wg, 0, wt) / D;
+        end = nt * share_prefix(wg + 1, 0, wt) / D;
+    }
+}
+// G == 0: the workgroup whose range holds tile t (the last w with beg(w) <= t)
+__device__ __forceinline__ int tile_wg(long long t, int ntph, int nt, int P) {
+    if (!xcd_weighted(ntph, nt, P, 0)) return (int)(((t + 1) * P - 1) / nt);
+    const long long D = share_prefix(P, 0, true);
+    const long long X = ((t + 1) * D - 1) / nt;   // the largest share prefix allowed
+    int w = (int)(X / kXcdShare);
+    if ((w & 1) && X % kXcdShare == 0) --w;       // share_prefix(w) = kXcdShare w + 1 > X
+    return w < P - 1 ? w : P - 1;
 }
 // the first workgroup owning a tile of head `head`, and how many own one
 __device__ __forceinline__ int head_wg_first(int head, int ntph, int nt, int P, int G) {
-    return G > 0 ? head * G : tile_wg((long long)head * ntph, nt, P);
+    return G > 0 ? head * G : tile_wg((long long)head * ntph, ntph, nt, P);
 }
 __device__ __forceinline__ int head_wg_count(int head, int ntph, int nt, int P, int G) {
     return G > 0 ? G
-                 : tile_wg((long long)head * ntph + ntph - 1, nt, P) - tile_wg((long long)head * ntph, nt, P) + 1;
+                 : tile_wg((long long)head * ntph + ntph - 1, ntph, nt, P) -
+                       tile_wg((long long)head * ntph, ntph, nt, P) + 1;
 }
 
 // Merge the partial top-s lists of head `head` (one per workgroup owning a
@@ -476,14 +518,7 @@ __global__ __launch_bounds__(kS2Waves *kWave) void heads_stage2_kernel(
         (&stage[0][0][0][0])[i] = make_float2(-INFINITY, __int_as_float(0x7FFFFFFF));
 
     long long wg_beg, wg_end;
-    if (G > 0) {
-        const int h = wg / G, j = wg % G;
-        wg_beg = (long long)h * ntph + (long long)j * ntph / G;
-        wg_end = (long long)h * ntph + (long long)(j + 1) * ntph / G;
-    } else {
-        wg_beg = (long long)wg * nt / P;
-        wg_end = (long long)(wg + 1) * nt / P;
-    }
+    wg_tiles(wg, ntph, nt, P, G, wg_beg, wg_end);
     const int head_lo = (int)(wg_beg / ntph);
     const long long span = wg_end - wg_beg;
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform

@@ -326,3 +326,89 @@ def test_heads_rows8_layout(kc, B, cg):
                 full = acc[q, lane, r] + acc[q, (lane + 40) % 64, r]
                 if v < rows:
                     assert abs(full - float(np.dot(W[v], z[col]))) < 1e-9
+
+
+# ------------------------------------------------- stage-2 workgroup split
+# Mirrors of the device formulas in heads.hip (wg_tiles, tile_wg,
+# head_wg_first / head_wg_count): the weighted split must cover every tile
+# once, in order, leave no workgroup empty, keep a workgroup within two heads
+# (its LDS holds two head slots), and the merge's inverse must name the owner
+# of every tile.
+XCD_SHARE = 32
+
+
+def _share_prefix(j, base, wt):
+    if not wt:
+        return j
+    return XCD_SHARE * j + ((-1 if base & 1 else 1) if j & 1 else 0)
+
+
+XCD_MIN_TILES = 32   # per wave, four waves per workgroup
+
+
+def _weighted(ntph, nt, P, G):
+    return ntph >= XCD_MIN_TILES * 4 * G if G > 0 else nt >= XCD_MIN_TILES * 4 * P
+
+
+def _wg_tiles(wg, ntph, nt, P, G):
+    wt = _weighted(ntph, nt, P, G)
+    if G > 0:
+        h, j = wg // G, wg % G
+        D = _share_prefix(G, h * G, wt)
+        return (h * ntph + ntph * _share_prefix(j, h * G, wt) // D,
+                h * ntph + ntph * _share_prefix(j + 1, h * G, wt) // D)
+    D = _share_prefix(P, 0, wt)
+    return nt * _share_prefix(wg, 0, wt) // D, nt * _share_prefix(wg + 1, 0, wt) // D
+
+
+def _tile_wg(t, ntph, nt, P):
+    if not _weighted(ntph, nt, P, 0):
+        return ((t + 1) * P - 1) // nt
+    D = _share_prefix(P, 0, True)
+    X = ((t + 1) * D - 1) // nt
+    w = X // XCD_SHARE
+    if (w & 1) and X % XCD_SHARE == 0:
+        w -= 1
+    return min(w, P - 1)
+
+
+@pytest.mark.parametrize("nh,ntph,cg", [(4, 4000, 1), (5, 16032, 1), (6, 16032, 1), (4, 125, 1),
+                                        (3, 64, 1), (17, 13, 1), (1, 2, 1), (5, 513, 1), (1, 32768, 1),
+                                        (2, 16385, 1), (16, 2049, 1), (1, 32769, 2),
+                                        (4, 4000, 2), (5, 4000, 2), (3, 377, 2), (2, 13, 2),
+                                        (17, 9000, 2), (1, 1, 2)])
+def test_stage2_workgroup_split(nh, ntph, cg):
+    nt = nh * ntph
+    if cg == 2:
+        G = max(1, min(256 // nh, ntph))
+        P = G * nh
+    else:
+        G, P = 0, min(nt, 256)
+    owner = {}
+    prev_end = 0
+    for wg in range(P):
+        beg, end = _wg_tiles(wg, ntph, nt, P, G)
+        if G > 0:
+            h = wg // G
+            assert beg >= h * ntph and end <= (h + 1) * ntph
+        assert beg < end, (wg, beg, end)            # never empty
+        if G == 0:
+            assert beg == prev_end                   # in order, no gap
+            assert (end - 1) // ntph - beg // ntph <= 1   # at most two heads
+        prev_end = end
+        for t in range(beg, end):
+            assert t not in owner
+            owner[t] = wg
+    assert len(owner) == nt
+    if G == 0:
+        for t in range(nt):
+            assert _tile_wg(t, ntph, nt, P) == owner[t]
+        for h in range(nh):
+            first = _tile_wg(h * ntph, ntph, nt, P)
+            last = _tile_wg(h * ntph + ntph - 1, ntph, nt, P)
+            assert {owner[t] for t in range(h * ntph, (h + 1) * ntph)} == set(range(first, last + 1))
+    # the weighting: even hardware ids take 33 shares per 31 of odd ones
+    if _weighted(ntph, nt, P, G) and G == 0 and P == 256:
+        ev = sum(_wg_tiles(w, ntph, nt, P, G)[1] - _wg_tiles(w, ntph, nt, P, G)[0] for w in range(0, P, 2))
+        od = nt - ev
+        assert 1.03 < ev / od < 1.09   # 33/31 up to the rounding of whole tiles
