@@ -70,6 +70,8 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05, s=None, w_lm_std=None):
     (16, 2, 1024, 20000, 4),   # 8-row tiles, all sixteen columns, many tiles per workgroup
     (9, 5, 640, 4099, 2),      # two column groups: one column in the second, leftover steps
     (10, 2, 512, 100, 3),      # two column groups, fewer tiles per head than workgroups
+    (4, 3, 512, 90001, 3),     # the XCD-weighted split (>= 32 tiles per wave), ragged last tile
+    (12, 1, 512, 262147, 2),   # XCD-weighted split within one head (two column groups)
 ])
 def test_heads_random_shapes(dtype, B, K, d, V, s):
     hx, ref, _ = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype, s=s)
