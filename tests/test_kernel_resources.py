@@ -13,6 +13,11 @@ buffer each stage is written to and read from, and when) is modelled step
 by step for prefetch depths 1 to 4: every stage computed must be the one
 its buffer holds, and no buffer may be overwritten before the barrier that
 follows its last read.
+
+The heads' stage-2 index arithmetic is modelled too: the 8-row tile's
+lane-to-(row, chunk) map, the LDS order of its B operand and the two-half
+sum against direct dot products, and the XCD-weighted split of the tiles
+over the workgroups with the inverse the merge kernel uses.
 """
 import os
 import re
