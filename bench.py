@@ -346,6 +346,22 @@ def measure_peaks(mv, dev, read_mib=2048, reps=10):
     ev[1].record()
     torch.cuda.synchronize()
     read_gbs = buf.numel() * 4 * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    # the same stream with per-workgroup clock stamps: workgroup w reads its
+    # share on XCD w mod 8, so the ends show each XCD's streaming time
+    # (pattern 0: linear; 1: 8-row tiles of 8 KiB rows, the heads' W2 pattern)
+    nwg = mv.lib.medusa_probe_read_workgroups()
+    mhz = mv.lib.medusa_probe_clock_mhz()
+    by_xcd = {}
+    for pattern, name in ((0, "linear"), (1, "rows8")):
+        stamps = torch.zeros(2 * nwg, dtype=torch.int32, device=dev)
+        mv.probe_read_timed(buf, sink, stamps, pattern)
+        mv.probe_read_timed(buf, sink, stamps, pattern)
+        torch.cuda.synchronize()
+        st = stamps.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        if mhz > 0:
+            t0 = st[0::2].min()
+            ends = ((st[1::2] - t0) % (1 << 32)) / mhz
+            by_xcd[name] = [round(float(np.median(ends[x::8])), 1) for x in range(8)]
     del buf
     iters = 16384
     mv.probe_mfma(iters, sink)
@@ -357,8 +373,12 @@ def measure_peaks(mv, dev, read_mib=2048, reps=10):
     torch.cuda.synchronize()
     tflops = flops / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
     return {"hbm_read_GBps": round(read_gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
+            "read_us_by_xcd": by_xcd or None,
             "method": f"medusa_probe_read over {read_mib} MiB x {reps}; medusa_probe_mfma "
-                      f"{iters} iterations x {reps} (events on the launch stream)"}
+                      f"{iters} iterations x {reps} (events on the launch stream); read_us_by_xcd: "
+                      f"the second of two medusa_probe_read_timed passes per pattern (linear; "
+                      f"8-row tiles of 8 KiB rows), the median end per XCD (workgroup w on XCD "
+                      f"w mod 8, an equal share each), microseconds from the first start"}
 
 
 def time_call(fn, steps, nbytes):

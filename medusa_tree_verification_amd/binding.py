@@ -33,7 +33,8 @@ EXPORTS = ["medusa_heads_topk", "medusa_heads_topk_root", "medusa_heads_stage1",
            "medusa_verify_forward", "medusa_verify_forward_workspace_bytes", "medusa_status_str",
            "medusa_abi_version"]
 PROBE_EXPORTS = ["medusa_probe_sink_bytes", "medusa_probe_read", "medusa_probe_mfma",
-                 "medusa_probe_mfma_flops"]
+                 "medusa_probe_mfma_flops", "medusa_probe_read_timed",
+                 "medusa_probe_read_workgroups", "medusa_probe_clock_mhz"]
 
 
 class MedusaError(RuntimeError):
@@ -79,6 +80,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.medusa_probe_sink_bytes.restype = Z
     L.medusa_probe_read.argtypes = [P, Z, P, P]
     L.medusa_probe_read.restype = I
+    L.medusa_probe_read_timed.argtypes = [P, Z, P, P, I, P]
+    L.medusa_probe_read_timed.restype = I
+    L.medusa_probe_read_workgroups.argtypes = []
+    L.medusa_probe_read_workgroups.restype = I
+    L.medusa_probe_clock_mhz.argtypes = []
+    L.medusa_probe_clock_mhz.restype = ctypes.c_double
     L.medusa_probe_mfma.argtypes = [I, P, P]
     L.medusa_probe_mfma.restype = I
     L.medusa_probe_mfma_flops.argtypes = [I]
@@ -378,6 +385,20 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     rc = lib.medusa_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                _stream(stream))
     _check("medusa_probe_read", rc)
+
+
+def probe_read_timed(buf: torch.Tensor, sink: torch.Tensor, stamps: torch.Tensor,
+                     pattern: int = 0, stream=None) -> None:
+    """A read pass (pattern 0: linear; 1: 8-row tiles of 8 KiB rows) that
+    records every workgroup's start and end clock in stamps (device int32, 2
+    per workgroup)."""
+    _need(buf, "buf")
+    _need(stamps, "stamps")
+    if stamps.numel() * stamps.element_size() < 8 * lib.medusa_probe_read_workgroups():
+        raise ValueError("stamps: 2 int32 per workgroup needed")
+    rc = lib.medusa_probe_read_timed(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     _ptr(stamps), int(pattern), _stream(stream))
+    _check("medusa_probe_read_timed", rc)
 
 
 def probe_mfma(iters: int, sink: torch.Tensor, stream=None) -> float:

@@ -351,9 +351,12 @@ __device__ __forceinline__ void stream_tile8(f32x4 (&acc)[CG], const T *__restri
 // workgroups in order, and tile t belongs to workgroup tile_wg(t).
 //
 // Workgroups are dispatched round-robin over the XCDs, so hardware id w runs
-// on XCD w mod 8, and the odd-numbered XCDs stream about 6% slower than the
-// even ones (measured on every box: per-wave end stamps, whichever part of
-// W2 they read).  So the shares are weighted: kXcdShare + 1 tiles' worth on
+// on XCD w mod 8, and the odd-numbered XCDs stream this access pattern (8-row
+// tiles of 8 KiB rows, whole lines) about 6% slower than the even ones:
+// per-wave end stamps on every box tried, whichever part of W2 they read,
+// and the rows8 pattern of medusa_probe_read_timed shows the same, while a
+// linear stream does not (so it follows from where these line addresses
+// fall in memory as seen from each XCD, not from the XCDs themselves).  So the shares are weighted: kXcdShare + 1 tiles' worth on
 // an even workgroup for every kXcdShare - 1 on an odd one, when every wave
 // gets kXcdMinTiles tiles or more.  With fewer the whole-tile rounding
 // decides (on 15-16 tiles per wave the slowest wave keeps its count and the

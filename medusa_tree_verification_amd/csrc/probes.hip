@@ -7,7 +7,15 @@
 //    (8 KiB of whole 128 B lines per wave) in flight: the fastest read shape
 //    measured (plain loads, or sixteen waves per CU, stream about 15% slower);
 //    the loaded words are folded into one value per thread so that no load
-//    can be dropped.
+//    can be dropped.  medusa_probe_read_timed also records each workgroup's
+//    start and end on the device's constant-rate clock: workgroups are
+//    dispatched round-robin over the XCDs, so workgroup w's share is read by
+//    XCD w mod 8, and the stamps show how fast each XCD streams.  Its second
+//    pattern reads the buffer as the heads' weight stream does: rows of
+//    8 KiB in tiles of 8 rows, each load 8 rows x 128 B (lane l: row
+//    (l mod 16) mod 8, 16 B at 64 ((l mod 16) / 8) + 16 (l / 16) of a 128 B
+//    step), a wave streaming a contiguous range of tiles in batches of 8
+//    steps.
 //  - medusa_probe_mfma: independent chains of v_mfma_f32_32x32x16_bf16 on
 //    register operands, four waves per CU (one per SIMD, eight accumulator
 //    chains each), no memory traffic in the loop.
@@ -23,8 +31,42 @@ constexpr int kProbeWG = kNumCU;    // one workgroup per CU, each streaming its 
 constexpr int kMfmaWaves = 4;       // one wave per SIMD ...
 constexpr int kMfmaChains = 8;      // ... with eight independent accumulator chains
 
+// the 8-row-tile pattern: a wave's share of the workgroup's tiles
+__device__ __forceinline__ uint32_t probe_tiles(const char *__restrict__ src, size_t ntile,
+                                                uint32_t acc) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int c = lane % 16, g = lane / 16;
+    const size_t lo = (size_t)blockIdx.x * ntile / gridDim.x, hi = (size_t)(blockIdx.x + 1) * ntile / gridDim.x;
+    const size_t t0 = lo + (hi - lo) * wave / (kProbeThreads / kWave);
+    const size_t t1 = lo + (hi - lo) * (wave + 1) / (kProbeThreads / kWave);
+    for (size_t t = t0; t < t1; ++t) {
+        const char *row = src + (t * 8 + c % 8) * 8192 + 64 * (c / 8) + 16 * g;
+        for (int b = 0; b < 8; ++b) {
+            u32x4 v[kProbeU];
+#pragma unroll
+            for (int u = 0; u < kProbeU; ++u) v[u] = ld16_nt(row + b * 1024 + u * 128);
+#pragma unroll
+            for (int u = 0; u < kProbeU; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+        }
+    }
+    return acc;
+}
+
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4 *__restrict__ src,
-                                                                   size_t n16, uint32_t *sink) {
+                                                                   size_t n16, uint32_t *sink,
+                                                                   uint32_t *stamps, int pattern) {
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    if (pattern == 1) {   // the same in every thread
+        const uint32_t acc = probe_tiles((const char *)src, n16 / 4096, 0u);
+        sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+            stamps[2 * blockIdx.x] = (uint32_t)t_start;
+            stamps[2 * blockIdx.x + 1] = (uint32_t)t_end;
+        }
+        return;
+    }
     // workgroup w streams its contiguous share; each of a wave's U loads
     // covers one kilobyte
     const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
@@ -42,6 +84,14 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4 *
         for (int u = 0; u < kProbeU; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
     sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+    if (stamps) {   // the same in every thread
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+            stamps[2 * blockIdx.x] = (uint32_t)t_start;
+            stamps[2 * blockIdx.x + 1] = (uint32_t)t_end;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kMfmaWaves *kWave) void probe_mfma_kernel(int iters, float *sink) {
@@ -81,12 +131,35 @@ extern "C" size_t medusa_probe_sink_bytes(void) {
     return rd > mf ? rd : mf;
 }
 
-extern "C" int medusa_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
+static int probe_read_launch(const void *buf, size_t bytes, void *sink, uint32_t *stamps,
+                             int pattern, void *stream) {
     if (!buf || !sink) return MEDUSA_ERR_NULL;
     if (bytes == 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0) return MEDUSA_ERR_SHAPE;
+    if (pattern == 1 && bytes % (8u * 8192u) != 0) return MEDUSA_ERR_SHAPE;
     hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeWG), dim3(kProbeThreads), 0,
-                       (hipStream_t)stream, (const u32x4 *)buf, bytes / 16, (uint32_t *)sink);
+                       (hipStream_t)stream, (const u32x4 *)buf, bytes / 16, (uint32_t *)sink,
+                       stamps, pattern);
     return hipGetLastError() == hipSuccess ? MEDUSA_OK : MEDUSA_ERR_LAUNCH;
+}
+
+extern "C" int medusa_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
+    return probe_read_launch(buf, bytes, sink, nullptr, 0, stream);
+}
+
+extern "C" int medusa_probe_read_timed(const void *buf, size_t bytes, void *sink, uint32_t *stamps,
+                                       int pattern, void *stream) {
+    if (!stamps) return MEDUSA_ERR_NULL;
+    if (pattern != 0 && pattern != 1) return MEDUSA_ERR_PARAM;
+    return probe_read_launch(buf, bytes, sink, stamps, pattern, stream);
+}
+
+extern "C" int medusa_probe_read_workgroups(void) { return kProbeWG; }
+
+extern "C" double medusa_probe_clock_mhz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0.0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0.0;
+    return khz / 1000.0;
 }
 
 extern "C" double medusa_probe_mfma_flops(int iters) {

@@ -55,6 +55,11 @@ def test_probe_validation(mv):
     assert L.medusa_probe_read(FAKE, 15, FAKE, None) == -2
     assert L.medusa_probe_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == -2
     assert L.medusa_probe_mfma(0, FAKE, None) == -6
+    assert L.medusa_probe_read_timed(FAKE, 16, FAKE, None, 0, None) == -1
+    assert L.medusa_probe_read_timed(FAKE, 15, FAKE, FAKE, 0, None) == -2
+    assert L.medusa_probe_read_timed(FAKE, 16, FAKE, FAKE, 2, None) == -6
+    assert L.medusa_probe_read_timed(FAKE, 4096, FAKE, FAKE, 1, None) == -2
+    assert L.medusa_probe_read_workgroups() == 256
     assert L.medusa_probe_mfma(1, None, None) == -1
     assert L.medusa_probe_mfma_flops(10) == 256 * 4 * 8 * 10 * 32 * 32 * 16 * 2
 
