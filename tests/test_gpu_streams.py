@@ -1,0 +1,122 @@
+"""GPU: every compute call runs on the stream it is given, and only there.
+
+The calls of one verify step (heads, tree attention, acceptance, KV commit,
+bonus-token draw) are enqueued on a side stream while the default stream is
+kept busy with unrelated work queued first.  Their outputs, pre-filled with
+a sentinel, are read back once the side stream's work has finished while
+the default stream is still busy (the test asserts that it is), and must
+equal bit for bit what the same calls wrote when run on the default stream.
+A launch that went to another stream would still be waiting behind the
+busy work (or would run before its inputs were ready) and leave sentinels or
+other values behind.  The values themselves are checked against the oracle
+by the other GPU tests; this file checks the stream plumbing."""
+import numpy as np
+import pytest
+
+from medusa_tree_verification_amd import workloads as W
+from tests.util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -7
+
+
+def _inputs():
+    import torch
+    B, K, d, V, s = 8, 2, 1024, 20000, 4
+    hx = {"hidden": to_dev(W.normal_tensor(901, (B, d), 1.0, "bf16")),
+          "w1": to_dev(W.normal_tensor(902, (K, d, d), 0.05, "bf16")),
+          "w2": to_dev(W.normal_tensor(903, (K, V, d), 0.05, "bf16"))}
+    tree = W.random_tree(904, 21, K, s)
+    logits = to_dev(W.normal_tensor(905, (B, tree.T, V), 2.0, "bf16"))
+    wl = W.WORKLOADS["ragged_b16_gqa_typical"]   # pipelined attention kernel plus the combine
+    ax = {k: to_dev(v) for k, v in W.attention_inputs(wl).items()}
+    at = W.workload_tree(wl)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda") % tree.T
+    u = torch.linspace(0.05, 0.95, B, device="cuda", dtype=torch.float32)
+    return dict(hx=hx, s=s, tree=tree, logits=logits, wl=wl, ax=ax, at=at, rows=rows, u=u)
+
+
+def _step(x, out, stream):
+    """The step's calls, writing into the preallocated tensors of out."""
+    from medusa_tree_verification_amd import binding as mv
+    hx, ax = x["hx"], x["ax"]
+    mv.medusa_heads_topk(hx["hidden"], hx["w1"], hx["w2"], x["s"], out=out["heads"],
+                         stream=stream)
+    mv.tree_attention(ax["q"], ax["k_cache"], ax["v_cache"], ax["prefix_len"], ax["k_tree"],
+                      ax["v_tree"], x["at"].parent, x["wl"].scale, out=out["attn"], stream=stream)
+    mv.tree_accept(x["logits"], out["heads"]["topk_ids"], x["tree"].parent, mv.TYPICAL, 0.7,
+                   out=out["accept"], stream=stream)
+    # commit the accepted path of each sequence into copies of the caches
+    mv.tree_commit_kv(out["kc"], out["vc"], out["plen"], ax["k_tree"], ax["v_tree"],
+                      out["best"], x["at"].parent, stream=stream)
+    mv.medusa_sample_token(x["logits"], x["rows"], x["u"], 0.7, token=out["token"],
+                           stream=stream)
+
+
+def _outputs(x):
+    """Output tensors filled with the sentinel (on the current stream)."""
+    import torch
+    hx, ax = x["hx"], x["ax"]
+    B, K, s = hx["hidden"].shape[0], hx["w2"].shape[0], x["s"]
+    T = x["tree"].T
+    i32 = dict(dtype=torch.int32, device="cuda")
+    Bt = ax["q"].shape[0]
+    return {
+        "heads": {"topk_ids": torch.full((B, K, s), SENTINEL, **i32),
+                  "topk_vals": torch.full((B, K, s), float(SENTINEL), device="cuda")},
+        "attn": torch.full_like(ax["q"], float(SENTINEL)),
+        "accept": {"accept_len": torch.full((B,), SENTINEL, **i32),
+                   "best_node": torch.full((B,), SENTINEL, **i32),
+                   "accepted_tokens": torch.full((B, K), SENTINEL, **i32),
+                   "node_tokens": torch.full((B, T), SENTINEL, **i32),
+                   "next_token": torch.full((B,), SENTINEL, **i32)},
+        "kc": ax["k_cache"].clone(), "vc": ax["v_cache"].clone(),
+        "plen": ax["prefix_len"].clone(),
+        # the deepest node of each sequence's tree as its accepted path end
+        "best": torch.full((Bt,), x["at"].T - 1, **i32),
+        "token": torch.full((B,), SENTINEL, **i32),
+    }
+
+
+def _flat(out):
+    """Every output as host bytes, in a fixed order."""
+    import torch
+    res = []
+    for k in sorted(out):
+        v = out[k]
+        for t in ([v[j] for j in sorted(v)] if isinstance(v, dict) else [v]):
+            res.append(t.contiguous().view(torch.uint8).cpu().numpy())
+    return res
+
+
+def test_calls_run_on_the_given_stream():
+    import torch
+    x = _inputs()
+    ref_out = _outputs(x)
+    _step(x, ref_out, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = _flat(ref_out)
+
+    side = torch.cuda.Stream()   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    # unrelated work queued on the default stream first (well over 100 ms)
+    a = torch.randn(4096, 4096, device="cuda")
+    for _ in range(150):
+        a = torch.mm(a, a) * 1e-3
+    busy_done = torch.cuda.Event()
+    busy_done.record()
+    with torch.cuda.stream(side):
+        out = _outputs(x)
+        _step(x, out, side)
+        step_done = torch.cuda.Event()
+        step_done.record()
+    step_done.synchronize()
+    # the check means something only while the default stream still works
+    assert not busy_done.query(), "the default stream finished first; lengthen its work"
+    with torch.cuda.stream(side):
+        got = _flat(out)   # copies on the side stream
+    assert len(got) == len(ref)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert np.array_equal(g, r), f"output {i} differs on the side stream"
+    torch.cuda.synchronize()
