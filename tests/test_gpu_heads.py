@@ -72,6 +72,9 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05, s=None, w_lm_std=None):
     (10, 2, 512, 100, 3),      # two column groups, fewer tiles per head than workgroups
     (4, 3, 512, 90001, 3),     # the XCD-weighted split (>= 32 tiles per wave), ragged last tile
     (12, 1, 512, 262147, 2),   # XCD-weighted split within one head (two column groups)
+    (1, 1, 16384, 3001, 3),    # the largest hidden size (rows past 8 KiB: 16-row tiles)
+    (2, 2, 8192, 4099, 8),     # 16 KiB (bf16) / 32 KiB (fp32) rows with the longest lists
+    (2, 16, 256, 1000, 3),     # the most heads
 ])
 def test_heads_random_shapes(dtype, B, K, d, V, s):
     hx, ref, _ = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype, s=s)
