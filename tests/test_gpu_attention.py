@@ -107,6 +107,19 @@ def test_attention_row_wave_counts(G, dtype):
     _check(x, t.parent, 1 / math.sqrt(dh), dtype)
 
 
+@pytest.mark.parametrize("G,dtype", [(2, "bf16"), (4, "bf16"), (4, "f32")])
+def test_attention_grid_over_several_rounds(G, dtype):
+    # more (sequence, kv head, m-tile) blocks than CUs: 23 sequences x 13 kv
+    # heads = 299 blocks, not a multiple of the eight XCDs, so the block
+    # remap's uneven ranges and a second round of workgroups both occur;
+    # prefixes 0..600 (G = 4, bf16: the pipelined kernel)
+    t = W.random_tree(70 + G, 64, 4, 3)
+    B, Hkv, dh, Lcap = 23, 13, 128, 600
+    L = [(37 * b) % 601 for b in range(B)]
+    x = _inputs(600 + G, B, G * Hkv, Hkv, t.T, dh, Lcap, L, dtype)
+    _check(x, t.parent, 1 / math.sqrt(dh), dtype)
+
+
 def test_attention_long_prefix_many_splits():
     t = TREES["full121"]
     B, Hq, Hkv, dh, Lcap = 1, 4, 1, 128, 20000
