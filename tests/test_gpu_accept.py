@@ -100,6 +100,32 @@ def test_accept_random(mode, dtype, V):
     _exact(g, ref, f"V={V}")
 
 
+@pytest.mark.parametrize("mode", ["greedy", "typical"])
+def test_accept_largest_tree_and_heads(mode):
+    # the most nodes (256), heads (16, so paths up to 16 deep) and top-s (8),
+    # and a 16-deep chain whose candidates are planted to be accepted
+    B, V = 5, 5000
+    for t, K, s in ((W.random_tree(78, 256, 16, 8), 16, 8), (W.chain_tree(16), 16, 1)):
+        rng = np.random.default_rng(t.T)
+        ids = np.stack([np.stack([rng.choice(V, s, replace=False) for _ in range(K)])
+                        for _ in range(B)]).astype(np.int32)
+        tok = W.path_tokens(t, ids)
+
+        def make(b, k, t=t, tok=tok):
+            r = np.random.default_rng([t.T, b, k])
+            raw = r.standard_normal((t.T, V)) * (3.0 if mode == "typical" else 1.0)
+            for n in range(1, t.T):   # candidates made likely (greedy: the first
+                # sibling made the argmax, so that paths run deep)
+                if r.random() < 0.9 and (mode == "typical" or t.paths[n][-1] == 0):
+                    raw[t.parent[n], tok[b, n]] = raw[t.parent[n]].max() + 0.5
+            return W.encode(raw, "bf16")
+
+        logits, ref = _redraw_knife_edges(make, ids, t.parent, "bf16", mode, 0.8, B)
+        g = _gpu(logits, ids, t.parent, mode, 0.8)
+        _exact(g, ref, f"T={t.T} K={K} s={s}")
+        assert ref["accept_len"].max() >= 4
+
+
 def test_accept_node_rank_and_trivial_trees():
     rng = np.random.default_rng(3)
     V, K, s = 50, 3, 4
