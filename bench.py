@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB read before each step of the per-call breakdown pass, outside "
                          "its events (more than the last-level cache and the L2s; 0: none)")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of whole steps run before the measured passes (unreported)")
     ap.add_argument("--forward-blocks", type=int, default=4,
                     help="attention blocks of the synthetic verify forward (a next-row timing)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -198,12 +200,40 @@ def main():
         if ev is not None:
             ev[5].record()
 
+    # Settle: whole steps for a fixed span of GPU time before any measured
+    # pass.  Right after an idle spell (here: the input set-up on the host)
+    # the attention's first few dozen calls run 7-17% slower while the
+    # chip's clock settles; the passes below then measure the steady state
+    # of a serving loop.  Nothing of this span is reported.
+    settle_steps = 0
+    t_settle = time.time()
+    while time.time() - t_settle < args.settle_s:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
+
+    # The per-call breakdown: a pass of the same steps with an event between
+    # calls (each event costs a little time of its own), every step starting
+    # with cold caches (a buffer larger than the last-level cache is read, a
+    # sum, before the step's first event; a read leaves no dirty lines, while
+    # after a written flush their write-back ran into the step's first
+    # kernels).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    flush = torch.ones(args.flush_mib << 17, dtype=torch.int64, device=dev) if args.flush_mib > 0 else None
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
+    for i in range(args.steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        step(evs[i])
+    torch.cuda.synchronize()
+    del flush, sink
+
+    # W untimed warm-up steps, then the K timed steps back to back with
+    # nothing else on the stream
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the timed steps run back to back with nothing else on the stream; the
-    # per-call breakdown comes from a second pass of the same steps with an
-    # event between calls (each event costs a little time of its own)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -213,19 +243,6 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    # each step of this pass starts with cold caches: a buffer larger than the
-    # last-level cache is read (a sum) before the step's first event.  A read
-    # leaves no dirty lines: after a written flush their write-back ran into
-    # the step's first kernels.
-    flush = torch.ones(args.flush_mib << 17, dtype=torch.int64, device=dev) if args.flush_mib > 0 else None
-    sink = torch.zeros((), dtype=torch.int64, device=dev)
-    for i in range(args.steps):
-        if flush is not None:
-            torch.sum(flush, dim=0, out=sink)
-        step(evs[i])
-    torch.cuda.synchronize()
-    del flush, sink
     names = ["heads_stage1", "heads_stage2", "heads_merge", "tree_attention", "tree_accept"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in
            enumerate(names)}
@@ -268,6 +285,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
