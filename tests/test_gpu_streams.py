@@ -38,15 +38,17 @@ def _inputs():
 
 
 def _step(x, out, stream):
-    """The step's calls, writing into the preallocated tensors of out."""
+    """The step's calls, writing into the preallocated tensors of out (and
+    using its preallocated workspaces: no allocation while they run)."""
     from medusa_tree_verification_amd import binding as mv
-    hx, ax = x["hx"], x["ax"]
+    hx, ax, ws = x["hx"], x["ax"], out["ws"]
     mv.medusa_heads_topk(hx["hidden"], hx["w1"], hx["w2"], x["s"], out=out["heads"],
-                         stream=stream)
+                         ws=ws["heads"], stream=stream)
     mv.tree_attention(ax["q"], ax["k_cache"], ax["v_cache"], ax["prefix_len"], ax["k_tree"],
-                      ax["v_tree"], x["at"].parent, x["wl"].scale, out=out["attn"], stream=stream)
+                      ax["v_tree"], x["at"].parent, x["wl"].scale, out=out["attn"],
+                      ws=ws["attn"], stream=stream)
     mv.tree_accept(x["logits"], out["heads"]["topk_ids"], x["tree"].parent, mv.TYPICAL, 0.7,
-                   out=out["accept"], stream=stream)
+                   out=out["accept"], ws=ws["accept"], stream=stream)
     # commit the accepted path of each sequence into copies of the caches
     mv.tree_commit_kv(out["kc"], out["vc"], out["plen"], ax["k_tree"], ax["v_tree"],
                       out["best"], x["at"].parent, stream=stream)
@@ -62,7 +64,16 @@ def _outputs(x):
     T = x["tree"].T
     i32 = dict(dtype=torch.int32, device="cuda")
     Bt = ax["q"].shape[0]
+    from medusa_tree_verification_amd import binding as mv
+    dt = mv.BF16
+    V, d = hx["w2"].shape[1], hx["w2"].shape[2]
+    Hq, Hkv, Lcap, dh = ax["q"].shape[1], ax["k_cache"].shape[1], ax["k_cache"].shape[2], ax["q"].shape[3]
+    ws = {"heads": mv.workspace(mv.lib.medusa_heads_topk_workspace_bytes(B, K, d, V, s, dt), "cuda"),
+          "attn": mv.workspace(mv.lib.tree_attention_workspace_bytes(Bt, Hq, Hkv, Lcap, dh,
+                                                                     x["at"].T, dt), "cuda"),
+          "accept": mv.workspace(mv.lib.tree_accept_workspace_bytes(B, T, V, K, s), "cuda")}
     return {
+        "ws": ws,
         "heads": {"topk_ids": torch.full((B, K, s), SENTINEL, **i32),
                   "topk_vals": torch.full((B, K, s), float(SENTINEL), device="cuda")},
         "attn": torch.full_like(ax["q"], float(SENTINEL)),
@@ -84,6 +95,8 @@ def _flat(out):
     import torch
     res = []
     for k in sorted(out):
+        if k == "ws":
+            continue
         v = out[k]
         for t in ([v[j] for j in sorted(v)] if isinstance(v, dict) else [v]):
             res.append(t.contiguous().view(torch.uint8).cpu().numpy())
@@ -100,14 +113,16 @@ def test_calls_run_on_the_given_stream():
 
     side = torch.cuda.Stream()   # default priority
     side.wait_stream(torch.cuda.current_stream())
-    # unrelated work queued on the default stream first (well over 100 ms)
+    with torch.cuda.stream(side):
+        out = _outputs(x)   # sentinel-filled, and every allocation made, beforehand
     a = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    # unrelated work queued on the default stream first (well over 100 ms)
     for _ in range(150):
         a = torch.mm(a, a) * 1e-3
     busy_done = torch.cuda.Event()
     busy_done.record()
     with torch.cuda.stream(side):
-        out = _outputs(x)
         _step(x, out, side)
         step_done = torch.cuda.Event()
         step_done.record()
