@@ -198,8 +198,11 @@ int medusa_heads_topk_root(const void *hidden, const void *w1, const void *w2, c
  *   mask_out    device [T][(T+63)/64] uint64 ancestor-or-self bit rows
  *               (bit j of word j/64 of row n), or NULL
  *
- * Limits: T <= 256, dh in {64, 128}, Hq % Hkv == 0, Hq/Hkv*T rows,
- * Lcap >= 0, scale > 0.  Arithmetic: MFMA (bf16 products, fp32
+ * Limits: T <= 256, dh in {64, 128}, Hq % Hkv == 0, Lcap >= 0,
+ * scale > 0; MEDUSA_ERR_SHAPE also when one kv head's query rows
+ * (Hq/Hkv*T*dh elements) reach 4 GiB, when B*Hkv*Lcap*dh reaches 2^40, or
+ * when the launch would need more than 2^31 - 1 workgroups (the workspace
+ * size is then 0).  Arithmetic: MFMA (bf16 products, fp32
  * accumulation; fp32 MFMA in F32 mode), online softmax in fp32.
  * ---------------------------------------------------------------------- */
 int tree_attention(const void *q, const void *k_cache, const void *v_cache,

@@ -1147,7 +1147,12 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int Lcap, int dh, int T, int dtype) {
         P.chunk = ch;
         P.nsplit = (Lcap + ch - 1) / ch;
     }
-    P.nwg = (int)(base * P.nsplit);
+    // grids past the launch limits (one-dimensional grids of at most
+    // 2^31 - 1 workgroups; the combine's eight rows per workgroup) are
+    // rejected by the caller: nwg = -1
+    const long long nwg = base * P.nsplit;
+    const long long nrows = (long long)B * Hq * T;
+    P.nwg = nwg <= 0x7FFFFFFFLL && (nrows + 7) / 8 <= 0x7FFFFFFFLL ? (int)nwg : -1;
     const size_t rows = (size_t)B * Hq * T;
     P.err_off = 0;
     P.o_off = 256;
@@ -1177,6 +1182,9 @@ int check_attn(const void *q, const void *kc, const void *vc, const int32_t *pl,
         T < 1 || T > MEDUSA_MAX_TREE)
         return MEDUSA_ERR_SHAPE;
     if ((long long)B * Hkv * Lcap * dh >= (1LL << 40)) return MEDUSA_ERR_SHAPE;
+    // the query rows of one kv head are read through one buffer resource
+    if ((long long)(Hq / Hkv) * T * dh * (dtype == MEDUSA_BF16 ? 2 : 4) >= (1LL << 32))
+        return MEDUSA_ERR_SHAPE;
     if (!(scale > 0.f) || scale != scale || scale == INFINITY) return MEDUSA_ERR_PARAM;
     return check_tree(parent, T);
 }
@@ -1216,7 +1224,9 @@ extern "C" size_t tree_attention_workspace_bytes(int B, int Hq, int Hkv, int Lca
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lcap < 0 || (dh != 64 && dh != 128) ||
         T < 1 || T > MEDUSA_MAX_TREE || (dtype != MEDUSA_F32 && dtype != MEDUSA_BF16))
         return 0;
-    return attn_plan(B, Hq, Hkv, Lcap, dh, T, dtype).total;
+    if ((long long)(Hq / Hkv) * T * dh * (dtype == MEDUSA_BF16 ? 2 : 4) >= (1LL << 32)) return 0;
+    const AttnPlan P = attn_plan(B, Hq, Hkv, Lcap, dh, T, dtype);
+    return P.nwg < 0 ? 0 : P.total;
 }
 
 extern "C" int tree_attention(const void *q, const void *k_cache, const void *v_cache,
@@ -1228,6 +1238,7 @@ extern "C" int tree_attention(const void *q, const void *k_cache, const void *v_
                         dh, T, scale, dtype, out);
     if (st != MEDUSA_OK) return st;
     const AttnPlan P = attn_plan(B, Hq, Hkv, Lcap, dh, T, dtype);
+    if (P.nwg < 0) return MEDUSA_ERR_SHAPE;
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < P.total) return MEDUSA_ERR_WORKSPACE;
     AttnParams p;
     p.q = q;

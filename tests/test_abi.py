@@ -130,6 +130,14 @@ def test_attention_validation(mv):
     assert call(parent=_i32([0, 0, 0, 1])) == -4          # root not -1
     assert call(parent=_i32([-1, 0, 3, 1])) == -4         # parent after child
     assert call(ws=None) == -5 and call(wsb=0) == -5
+    # grids past the launch limits and query blocks past one buffer resource
+    big = dict(Hq=1 << 16, Hkv=1 << 16)
+    assert L.tree_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, par, 1 << 16, big["Hq"],
+                            big["Hkv"], 0, 128, 4, 0.1, 1, FAKE, None, FAKE_WS, 1 << 40,
+                            None) == -2
+    assert L.tree_attention_workspace_bytes(1 << 16, 1 << 16, 1 << 16, 0, 128, 4, 1) == 0
+    assert call(Hq=1 << 22, Hkv=1) == -2
+    assert L.tree_attention_workspace_bytes(1, 1 << 22, 1, 64, 128, 4, 1) == 0
 
 
 def test_accept_validation(mv):
