@@ -351,18 +351,20 @@ __device__ __forceinline__ void stream_tile8(f32x4 (&acc)[CG], const T *__restri
 // workgroups in order, and tile t belongs to workgroup tile_wg(t).
 //
 // Workgroups are dispatched round-robin over the XCDs, so hardware id w runs
-// on XCD w mod 8, and the odd-numbered XCDs stream this access pattern (8-row
-// tiles of 8 KiB rows, whole lines) about 6% slower than the even ones:
-// per-wave end stamps on every box tried, whichever part of W2 they read,
-// and the rows8 pattern of medusa_probe_read_timed shows the same, while a
-// linear stream does not (so it follows from where these line addresses
-// fall in memory as seen from each XCD, not from the XCDs themselves).  So the shares are weighted: kXcdShare + 1 tiles' worth on
-// an even workgroup for every kXcdShare - 1 on an odd one, when every wave
-// gets kXcdMinTiles tiles or more.  With fewer the whole-tile rounding
-// decides (on 15-16 tiles per wave the slowest wave keeps its count and the
-// even XCDs only get more: llama7b_b1 stage 2 1.6 us slower, against 17 us
-// faster on large_vocab_typical's 78 tiles per wave).  share_prefix(j, base)
-// is the summed share of workgroups base .. base + j - 1.
+// on XCD w mod 8 (the XCC id register agrees on every launch checked), and
+// the odd-numbered XCDs stream this access pattern (8-row tiles of 8 KiB
+// rows, whole lines) 6-9% slower than the even ones when all read at once:
+// the 8-row pattern of medusa_probe_read_timed shows it, a linear stream does
+// not.  The shares are weighted accordingly: kXcdShare + 1 tiles' worth on an
+// even workgroup for every kXcdShare - 1 on an odd one, when every wave gets
+// kXcdMinTiles tiles or more.  Same-box runs on large_vocab_typical found no
+// effect of the weights themselves: with the shares inverted, or with the
+// weighting switched off in this code, the stream took 730-733 us either way
+// (the XCDs that finish early leave their share of the HBM bandwidth to the
+// others).  A rewrite of these functions without the weighting ran 2.5%
+// slower with an unchanged main loop, so this form stays, as the fastest
+// build measured.  share_prefix(j, base) is the summed share of workgroups
+// base .. base + j - 1.
 constexpr int kXcdShare = 32;
 constexpr int kXcdMinTiles = 32;
 __device__ __forceinline__ long long share_prefix(int j, int base, bool wt) {
