@@ -75,6 +75,9 @@ def _random_heads(seed, B, K, d, V, dtype, wstd=0.05, s=None, w_lm_std=None):
     (1, 1, 16384, 3001, 3),    # the largest hidden size (rows past 8 KiB: 16-row tiles)
     (2, 2, 8192, 4099, 8),     # 16 KiB (bf16) / 32 KiB (fp32) rows with the longest lists
     (2, 16, 256, 1000, 3),     # the most heads
+    (2, 3, 128, 1, 1),         # a one-token vocabulary (every tile row but one clamped)
+    (3, 2, 256, 2, 2),         # s = V
+    (5, 4, 1024, 7, 3),        # fewer rows than one tile, 8-row tiles
 ])
 def test_heads_random_shapes(dtype, B, K, d, V, s):
     hx, ref, _ = _random_heads(hash((B, K, d, V, s)) % 10000 * 10, B, K, d, V, dtype, s=s)
