@@ -653,15 +653,19 @@ __global__ __launch_bounds__(NW *kWave, 1) void tree_attn_fwd_kernel(AttnParams 
 // transpose reads (4 key rows x 64 bytes per 32 lanes) hit distinct banks.
 //
 // Per wave the 32-key blocks form a pipeline: block j + 1's scores are
-// computed on the matrix cores while block j's row max is found, and the
-// P V product of block j's first 16 keys runs while the second 16 are
-// exponentiated.  Blocks past a stage boundary come from the next stage's
+// computed on the matrix cores while block j's row max is found (first
+// half of the k-steps) and its first 16 keys are exponentiated (second
+// half), and the P V product of block j's first 16 keys runs while the
+// second 16 are exponentiated.  Blocks past a stage boundary come from the next stage's
 // buffer, which the previous barrier made visible; one barrier per stage.
 constexpr int kPipeNB = 4;                                     // LDS stage buffers
 constexpr int kPipeRB = 128 * 2;                               // bytes per K or V row
 constexpr int kPipeOp = kBN * kPipeRB;                         // one operand of one stage
 constexpr int kPipeLoads = 2 * (kPipeOp / 1024) / kMaxWaves;   // loads per wave and stage
 static_assert(kPipeLoads == 4, "the stage wait below counts four loads per wave");
+
+// instruction classes of the scheduler's group barriers
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgTrans = 0x400;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
@@ -709,14 +713,29 @@ __device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, u
         for (int r = 0; r < 16; ++r)
             sc[r] = (bits >> (8 * (r >> 2) + (r & 3))) & 1u ? sc[r] : -INFINITY;
     }
-    // the next block's scores start from -m (the reference as it is now)
+    // the next block's scores start from -m (the reference as it is now):
+    // its first four k-steps go out before this block's row max, the last
+    // four after the reference check, beside this block's exponentials
+    // (their K fragments are read now)
     sn = mma32_first(st.negr, pipe_ld16(kbuf, pl.ka[0] + koff), qf[0], bf16_t{});
 #pragma unroll
-    for (int ks = 1; ks < 8; ++ks) mma32_step(sn, pipe_ld16(kbuf, pl.ka[ks] + koff), qf[ks], bf16_t{});
+    for (int ks = 1; ks < 4; ++ks) mma32_step(sn, pipe_ld16(kbuf, pl.ka[ks] + koff), qf[ks], bf16_t{});
+    u32x4 kr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = pipe_ld16(kbuf, pl.ka[4 + i] + koff);
     float mx = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
     mx = pair_max(mx);
+    // issue order up to the reference check: the eight K fragment reads,
+    // then each of the first four k-steps followed by four of the row-max
+    // operations
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 1);
+    }
     // lazy reference (as in attend_stage, with the threshold kept in st.thr);
     // a move also applies to the next block's scores, which were taken
     // against the old one
@@ -738,6 +757,10 @@ __device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, u
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.negr[r] = nr;
     }
+    // the rest of the next block's k-steps (a reference move above applied
+    // to the part already summed, which the rest adds to unchanged)
+#pragma unroll
+    for (int ks = 4; ks < 8; ++ks) mma32_step(sn, kr[ks - 4], qf[ks], bf16_t{});
     // probabilities packed to bf16 for the P V product (k-step mm: keys
     // 16 mm + 4h + 8 (e / 4) + e % 4 in element e of the B operand); the row
     // sum takes the same bf16 values
@@ -762,6 +785,30 @@ __device__ __forceinline__ void pipe_block(const char *kbuf, const char *vbuf, u
         }
     }
     st.l = acc;
+    // issue order after the reference check:
+    //   the V^T reads of keys 0-15;
+    //   the last four k-steps of the next block's scores, each followed by
+    //   two exponentials of keys 0-15;
+    //   the V^T reads of keys 16-31;
+    //   the four P V products of keys 0-15, each followed by two
+    //   exponentials of keys 16-31;
+    //   the four P V products of keys 16-31.
+    // Left to itself the compiler issues each group of matrix products back
+    // to back and the exponentials only after them, so that the matrix
+    // cores wait on this wave's exponentials.
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 4, 0);
 }
 
 // The four stage buffers, K and V (16 KiB each), as separate LDS variables
