@@ -127,6 +127,36 @@ def test_attention_long_prefix_many_splits():
     _check(x, t.parent, 1 / math.sqrt(dh), "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_reference_moves(dtype):
+    # Scores (log2 units) that step up by 9 per 32-key block over the first
+    # six blocks and then stay level: every step lifts the block maximum past
+    # the running reference + 8, so the kernels move their reference five
+    # times while the next block's q.k products are partly summed, and the
+    # blocks after the last move carry nearly all of the softmax weight, so a
+    # wrong correction of that partial sum would show in the output.  G * T =
+    # 256 rows per kv head (bf16: the pipelined kernel).
+    t = W.random_tree(91, 64, 4, 3)
+    B, Hkv, G, dh, Lcap = 2, 2, 4, 128, 700
+    L = [700, 389]
+    Hq, T = G * Hkv, t.T
+    scale = 1 / math.sqrt(dh)
+    c = scale * math.log2(math.e)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([4242])))
+    u = rng.standard_normal(dh).astype(np.float32)
+    q = u + 0.1 * rng.standard_normal((B, Hq, T, dh)).astype(np.float32)
+    step = 9.0 * np.minimum(np.arange(Lcap) // 32, 5).astype(np.float32)
+    k = 0.3 * rng.standard_normal((B, Hkv, Lcap, dh)).astype(np.float32)
+    k += (step / (c * float(u @ u)))[None, None, :, None] * u
+    conv = (lambda a: W.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    x = dict(q=conv(q), k_cache=conv(k),
+             v_cache=conv(rng.standard_normal((B, Hkv, Lcap, dh)).astype(np.float32)),
+             k_tree=conv(rng.standard_normal((B, Hkv, T, dh)).astype(np.float32)),
+             v_tree=conv(rng.standard_normal((B, Hkv, T, dh)).astype(np.float32)),
+             prefix_len=np.asarray(L, np.int32))
+    _check(x, t.parent, scale, dtype)
+
+
 def test_attention_prefix_out_of_range_is_clamped_and_flagged():
     from medusa_tree_verification_amd import binding as mv
     import torch
